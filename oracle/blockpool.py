@@ -1,0 +1,131 @@
+"""Block pool model: free queue, reference counts, immediate release.
+
+Page 1, "KV cache: Generation state, latency, and allocation", section 21.5,
+Table 21.1 and the five numbered steps after it:
+
+* the pool is a fixed set of physical block ids, each with ``block_size``
+  position slots (page 2, section "Why PagedAttention allocates KV in
+  blocks": the pool is initialised up front with a free-block queue);
+* allocation takes a free block and records it in the request's table
+  (step 2);
+* sharing a complete block into another table raises its reference count
+  (step 3, count two);
+* releasing a request removes its references; a block whose count reaches
+  zero returns to the free pool at once (step 4, "immediate-release
+  policy"), while a block still referenced stays live (step 4, block 7);
+* a shared block that is only partly filled must not be written in place
+  (copy-on-write paragraph after the walk); this model reports that case as
+  an error instead of copying.
+
+The free pool is a FIFO queue: ``alloc`` pops the head, a release pushes to
+the tail.  The pages call it a "free pool", a "free-block queue" (page 2) and
+a "free list" (page 3) without fixing an order; FIFO is the plain reading.
+"""
+
+from __future__ import annotations
+
+from collections import deque
+
+
+class PoolError(Exception):
+    """Base class; ``code`` mirrors the status names of the C library."""
+    code = "error"
+
+
+class OutOfBlocks(PoolError):
+    code = "out_of_blocks"
+
+
+class BadBlock(PoolError):
+    code = "bad_block"
+
+
+class SharedBlock(PoolError):
+    code = "shared_block"
+
+
+class InvalidArg(PoolError):
+    code = "invalid_arg"
+
+
+class BlockPool:
+    def __init__(self, num_blocks: int, block_size: int, free_order=None):
+        if num_blocks <= 0 or block_size <= 0:
+            raise InvalidArg("num_blocks and block_size must be positive")
+        if free_order is None:
+            free_order = list(range(num_blocks))
+        free_order = [int(x) for x in free_order]
+        if sorted(free_order) != list(range(num_blocks)):
+            raise InvalidArg("free_order must be a permutation of 0..num_blocks-1")
+        self.num_blocks = num_blocks
+        self.block_size = block_size
+        self.free = deque(free_order)
+        self.refcount = [0] * num_blocks
+
+    # ---- block level -----------------------------------------------------
+    def alloc(self) -> int:
+        if not self.free:
+            raise OutOfBlocks("no free block")
+        b = self.free.popleft()
+        self.refcount[b] = 1
+        return b
+
+    def _check(self, b: int):
+        if not (0 <= b < self.num_blocks) or self.refcount[b] == 0:
+            raise BadBlock(f"block {b} is not live")
+
+    def incref(self, b: int):
+        self._check(b)
+        self.refcount[b] += 1
+
+    def decref(self, b: int):
+        self._check(b)
+        self.refcount[b] -= 1
+        if self.refcount[b] == 0:
+            self.free.append(b)
+
+    def num_free(self) -> int:
+        return len(self.free)
+
+    def num_used(self) -> int:
+        return self.num_blocks - len(self.free)
+
+    # ---- sequence level --------------------------------------------------
+    def prepare_append(self, table_row: list, ctx_before: int) -> tuple:
+        """Make room for the position ``ctx_before`` (zero-based) of one
+        request whose table row is ``table_row`` (a Python list that grows).
+
+        Returns (physical block, slot) of the new position.  A new block is
+        taken iff the position opens a new logical block (page 1, section
+        21.5, step 2); writing into a block with refcount > 1 is refused
+        (copy-on-write paragraph)."""
+        bs = self.block_size
+        j, r = divmod(ctx_before, bs)
+        if r == 0:
+            if len(table_row) != j:
+                raise InvalidArg("table row length does not match ctx_before")
+            table_row.append(self.alloc())
+        else:
+            if len(table_row) != j + 1:
+                raise InvalidArg("table row length does not match ctx_before")
+        b = table_row[j]
+        if self.refcount[b] > 1:
+            raise SharedBlock(f"block {b} is shared (refcount {self.refcount[b]})")
+        return b, r
+
+    def share_prefix(self, src_row: list, n_full_blocks: int) -> list:
+        """Map the first ``n_full_blocks`` complete blocks of ``src_row`` into
+        a new table row (page 1, section 21.5, step 3)."""
+        if n_full_blocks > len(src_row):
+            raise InvalidArg("not that many blocks in the source row")
+        dst = []
+        for j in range(n_full_blocks):
+            self.incref(src_row[j])
+            dst.append(src_row[j])
+        return dst
+
+    def release(self, table_row: list):
+        """Drop one reference to every block of a finished request (page 1,
+        section 21.5, steps 4 and 5)."""
+        for b in table_row:
+            self.decref(b)

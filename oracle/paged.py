@@ -1,0 +1,155 @@
+"""Paged decode step: slot mapping, append, gather, exact attention (float64).
+
+Sources on the pages (page 1 = "KV cache: Generation state, latency, and
+allocation"; page 3 = "xf_kv_cache"):
+
+* Slot mapping -- page 1, section 21.5: position t of a request lies in
+  logical block floor(t / bs) at slot t mod bs, and the request's block table
+  gives the physical block.
+* Append -- page 1, section 21.6, Eq. 21.6: each decode pass appends the
+  consumed token's K and V to the cache, keeping logical order; section
+  21.1: the new query reads the cached keys *and its own new key*.  So the
+  append happens first and attention covers n_b positions, where n_b counts
+  the positions after the append.
+* Validity -- page 1, section 21.1 (after Eq. 21.1): unused slots must never
+  be read as keys; section 21.5: occupancy marks valid slots.  Positions
+  >= n_b are never gathered.
+* Grouped heads -- page 1, section 21.1: H_Q must be divisible by H_KV and
+  every query head keeps its own scores.  Query head hq reads KV head
+  floor(hq / g), g = H_Q / H_KV (contiguous groups; the pages leave the
+  assignment open).
+* Attention -- page 1, section 21.1: scores are normalised and mix the
+  values.  With scale c: s_t = c * q . k_t, w_t = exp(s_t - max s),
+  out = sum_t w_t v_t / sum_t w_t.  Subtracting the maximum changes nothing
+  mathematically and keeps exp() in range.
+
+Storage formats (``kv_dtype``): "f32" (float32 arrays), "bf16" (uint16 bit
+patterns), "fp8_e4m3" (uint8 codes with one float32 scale per (physical
+block, KV head); stored value = code value * scale).  Query and new-token
+inputs are "f32" or "bf16".  Pools are laid out [num_blocks, H_KV, bs, d_h]
+for K and V separately.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+from . import codecs
+
+F32, BF16, FP8 = "f32", "bf16", "fp8_e4m3"
+
+
+def _in_to_f64(x, dtype: str) -> np.ndarray:
+    if dtype == F32:
+        return np.asarray(x, dtype=np.float32).astype(np.float64)
+    if dtype == BF16:
+        return codecs.bf16_bits_to_f64(x)
+    raise ValueError(f"unsupported input dtype {dtype}")
+
+
+def slot_of(block_table_row, position: int, block_size: int) -> tuple:
+    """(physical block, slot) holding zero-based logical ``position``."""
+    j, r = divmod(int(position), int(block_size))
+    return int(block_table_row[j]), r
+
+
+def append(k_cache, v_cache, kv_dtype: str, k_new, v_new, in_dtype: str,
+           block_table, context_lens, block_size: int,
+           k_scale=None, v_scale=None):
+    """Write each request's new K, V into slot (n_b - 1); return new pools.
+
+    Stored form: the same bits for f32 -> f32 and bf16 -> bf16; for fp8, the
+    E4M3FN code of fp32(x) / scale[p, h] (see ``codecs``).  Every other pool
+    byte is left untouched."""
+    kc = np.array(k_cache, copy=True)
+    vc = np.array(v_cache, copy=True)
+    num_blocks = kc.shape[0]
+    B, H_KV, _ = np.shape(k_new)
+    for b in range(B):
+        n = int(context_lens[b])
+        if n < 1:
+            raise ValueError("context length after append must be >= 1")
+        p, r = slot_of(block_table[b], n - 1, block_size)
+        if not 0 <= p < num_blocks:
+            raise ValueError(f"block id {p} outside the pool")
+        for h in range(H_KV):
+            for src, dst, sc in ((k_new, kc, k_scale), (v_new, vc, v_scale)):
+                x = np.asarray(src[b, h])
+                if kv_dtype == in_dtype:
+                    dst[p, h, r, :] = x
+                elif kv_dtype == FP8:
+                    xf = _in_to_f64(x, in_dtype).astype(np.float32)  # exact
+                    dst[p, h, r, :] = codecs.e4m3_quantize(xf, np.float32(sc[p, h]))
+                else:
+                    raise ValueError(f"unsupported append {in_dtype} -> {kv_dtype}")
+    return kc, vc
+
+
+def decode_stored(pool_slice, kv_dtype: str, scale=None) -> np.ndarray:
+    """Stored scalars -> float64 values (exact)."""
+    if kv_dtype == F32:
+        return np.asarray(pool_slice, dtype=np.float32).astype(np.float64)
+    if kv_dtype == BF16:
+        return codecs.bf16_bits_to_f64(pool_slice)
+    if kv_dtype == FP8:
+        return codecs.e4m3_decode(pool_slice) * float(scale)
+    raise ValueError(f"unsupported kv dtype {kv_dtype}")
+
+
+def gather_head(cache, kv_dtype: str, scale, table_row, n: int, h: int,
+                block_size: int) -> np.ndarray:
+    """Dense float64 [n, d_h] keys (or values) of KV head ``h`` of one request,
+    in logical order, read through its table: the paged form turned back into
+    Eq. 21.1's layout for B = 1 and T = n."""
+    t = np.arange(n)
+    p = np.asarray(table_row, dtype=np.int64)[t // block_size]   # physical block per position
+    r = t % block_size                                           # slot per position
+    if kv_dtype == FP8:
+        return codecs.e4m3_decode(cache[p, h, r]) * np.asarray(scale, np.float64)[p, h][:, None]
+    return decode_stored(cache[p, h, r], kv_dtype)
+
+
+def attend_one(q_rows, K, V, softmax_scale: float) -> np.ndarray:
+    """Exact softmax attention of several query rows over one key/value set.
+
+    q_rows [g, d], K [n, d], V [n, d] (float64) -> [g, d]."""
+    s = (q_rows @ K.T) * softmax_scale                      # [g, n]
+    w = np.exp(s - s.max(axis=1, keepdims=True))
+    return (w @ V) / w.sum(axis=1, keepdims=True)
+
+
+def attend(q, q_dtype: str, k_cache, v_cache, kv_dtype: str, block_table,
+           context_lens, block_size: int, softmax_scale: float,
+           k_scale=None, v_scale=None, requests=None) -> np.ndarray:
+    """float64 output [B, H_Q, d_h] of one decode query per request.
+
+    ``requests`` optionally restricts the computation to some request
+    indices (the others are left as NaN), for sampled checks at full size."""
+    qf = _in_to_f64(q, q_dtype)
+    B, H_Q, d_h = qf.shape
+    H_KV = k_cache.shape[1]
+    if H_Q % H_KV:
+        raise ValueError("H_Q must be divisible by H_KV")
+    g = H_Q // H_KV
+    out = np.full((B, H_Q, d_h), np.nan, dtype=np.float64)
+    for b in (range(B) if requests is None else requests):
+        n = int(context_lens[b])
+        for h in range(H_KV):
+            K = gather_head(k_cache, kv_dtype, k_scale, block_table[b], n, h, block_size)
+            V = gather_head(v_cache, kv_dtype, v_scale, block_table[b], n, h, block_size)
+            out[b, h * g:(h + 1) * g] = attend_one(qf[b, h * g:(h + 1) * g], K, V,
+                                                    softmax_scale)
+    return out
+
+
+def decode_step(q, q_dtype, k_new, v_new, k_cache, v_cache, kv_dtype,
+                block_table, context_lens, block_size, softmax_scale,
+                k_scale=None, v_scale=None, requests=None):
+    """Append, then attend (page 1, section 21.1 and Eq. 21.6).
+
+    Returns (k_cache_after, v_cache_after, out)."""
+    kc, vc = append(k_cache, v_cache, kv_dtype, k_new, v_new, q_dtype,
+                    block_table, context_lens, block_size, k_scale, v_scale)
+    out = attend(q, q_dtype, kc, vc, kv_dtype, block_table, context_lens,
+                 block_size, softmax_scale, k_scale, v_scale, requests)
+    return kc, vc, out
