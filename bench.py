@@ -1,0 +1,250 @@
+"""Benchmark of one paged decode step on one MI355X.
+
+A step is the whole hot path for one batch: kv_append of every request's
+new K/V, then paged decode attention (partition kernel + split-K combine)
+for one layer (or every layer of the ``shared_prefix`` workload).  Inputs are
+seeded synthetic draws resident in HBM before the timed region.  To keep the
+256 MB last-level cache from serving repeated reads, single-layer workloads
+rotate over ``--rotate`` copies of the KV pools (same tables, different
+buffers); the 32-layer workload rotates by itself.
+
+Prints ONE JSON line on stdout (diagnostics go to stderr).  ``value`` is the
+achieved algorithmic GB/s of the whole step; ``roofline`` reports the
+partition kernel alone, timed with HIP events on the stream it runs on;
+``cpu_baseline`` times the float64 CPU oracle on a bounded sample of the
+same workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "paged GQA decode attn: achieved HBM GB/s (% of peak) + µs/step per layer"
+PEAK_GBS = 8000.0   # MI355X HBM3E, vendor figure
+KERNEL_SOURCES = ["decode_mfma.hip", "decode_generic.hip", "pkv_device.h"]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_digest() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "paged_kv_cache_105_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str, partition: int):
+    """HBM bytes per launch of the partition kernel from the committed
+    rocprofv3 counter summary, if it was taken on the current kernel source."""
+    path = os.path.join(ROOT, "profiles", f"pmc_decode_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    m = re.search(r"```json\n(.*?)\n```", open(path).read(), re.S)
+    if not m:
+        return None
+    rec = json.loads(m.group(1))
+    if rec.get("kernel_source_digest") != kernel_source_digest():
+        return None
+    if rec.get("partition_tokens") != partition:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, layer_tensors, budget_s: float):
+    """Time the oracle (as it stands) on a bounded sample: the append of the
+    whole batch, then attention request by request until ~budget_s."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    from oracle import paged
+    from paged_kv_cache_105_amd import metrics
+    from paged_kv_cache_105_amd.workloads import as_numpy
+
+    q, kn, vn, kc, vc, ks, vs = layer_tensors
+    d = dict(q=as_numpy(q), kn=as_numpy(kn), vn=as_numpy(vn), kc=as_numpy(kc).copy(),
+             vc=as_numpy(vc).copy(), table=as_numpy(w.block_table), lens=as_numpy(w.context_lens),
+             ks=None if ks is None else as_numpy(ks), vs=None if vs is None else as_numpy(vs))
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        paged.append(d["kc"], d["vc"], w.kv_dtype, d["kn"], d["vn"], w.q_dtype, d["table"],
+                     d["lens"], w.block_size, d["ks"], d["vs"], inplace=True)
+        done = []
+        for b in range(w.B):
+            paged.attend(d["q"], w.q_dtype, d["kc"], d["vc"], w.kv_dtype, d["table"], d["lens"],
+                         w.block_size, w.softmax_scale, d["ks"], d["vs"], requests=[b])
+            done.append(b)
+            if time.perf_counter() - t0 > budget_s:
+                break
+        dt = time.perf_counter() - t0
+    lens = [int(d["lens"][b]) for b in done]
+    nbytes = metrics.append_bytes(w.B, w.H_KV, w.d_h, w.kv_dtype, w.q_dtype) + \
+        metrics.attention_bytes(lens, w.H_Q, w.H_KV, w.d_h, w.block_size, w.kv_dtype,
+                                w.q_dtype)["total"]
+    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"one layer: append of all {w.B} requests + attention of {len(done)} of "
+                      f"{w.B} requests ({sum(lens)} positions), float64 numpy, BLAS pinned to "
+                      f"1 thread, {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="llama8b")
+    ap.add_argument("--partition", type=int, default=0, help="positions per partition, 0 = default")
+    ap.add_argument("--rotate", type=int, default=4, help="KV pool copies for cold-cache timing")
+    ap.add_argument("--variant", type=int, default=0, help="0 auto, 1 generic, 2 mfma")
+    ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        log(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported")
+        sys.exit(2)
+
+    import torch
+
+    import paged_kv_cache_105_amd as pkv
+    from paged_kv_cache_105_amd import metrics
+    from paged_kv_cache_105_amd.workloads import make_workload
+
+    pkv.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    t_gen = time.perf_counter()
+    w = make_workload(args.workload, device=dev)
+    lens = w.context_lens.cpu().tolist()
+    log(f"workload {args.workload}: B={w.B} H_Q={w.H_Q} H_KV={w.H_KV} d_h={w.d_h} "
+        f"bs={w.block_size} kv={w.kv_dtype} layers={w.layers} blocks={w.num_blocks} "
+        f"max_len={w.max_context_len} (generated in {time.perf_counter() - t_gen:.1f} s)")
+
+    # pools per (rotation, layer)
+    R = max(1, args.rotate) if w.layers == 1 else 1
+    pools = []
+    for r in range(R):
+        pools.append([(w.k_cache[L] if r == 0 else w.k_cache[L].clone(),
+                       w.v_cache[L] if r == 0 else w.v_cache[L].clone()) for L in range(w.layers)])
+    pt, parts, ws_bytes = pkv.decode_plan(w.B, w.H_Q, w.H_KV, w.d_h, w.block_size,
+                                          w.max_context_len, args.partition)
+    work = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+    out = torch.empty((w.B, w.H_Q, w.d_h), dtype=torch.float32, device=dev)
+    pkv.set_decode_variant(args.variant)
+    stream = torch.cuda.current_stream()
+    ks = w.k_scale or [None] * w.layers
+    vs = w.v_scale or [None] * w.layers
+
+    def step(r, events=None):
+        for L in range(w.layers):
+            kc, vc = pools[r][L]
+            pkv.kv_append(w.k_new[L], w.v_new[L], kc, vc, w.block_table, w.context_lens,
+                          ks[L], vs[L], stream=stream)
+            if events is not None:
+                events[0].record(stream)
+            pkv.decode_partitions(out, w.q[L], kc, vc, w.block_table, w.context_lens,
+                                  w.max_context_len, w.softmax_scale, ks[L], vs[L],
+                                  partition_tokens=pt, workspace=work, stream=stream)
+            if events is not None:
+                events[1].record(stream)
+            pkv.combine_partitions(out, w.context_lens, w.max_context_len, w.H_KV,
+                                   w.block_size, partition_tokens=pt, workspace=work,
+                                   stream=stream)
+
+    for i in range(args.warmup):
+        step(i % R)
+    torch.cuda.synchronize()
+
+    # timed region 1: wall clock over K steps, no extra events
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i % R)
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
+
+    # timed region 2: same steps with HIP events around every partition launch
+    evs = [[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
+           for _ in range(args.steps * w.layers)]
+    torch.cuda.synchronize()
+    k = 0
+    for i in range(args.steps):
+        for L in range(w.layers):
+            kc, vc = pools[i % R][L]
+            pkv.kv_append(w.k_new[L], w.v_new[L], kc, vc, w.block_table, w.context_lens,
+                          ks[L], vs[L], stream=stream)
+            evs[k][0].record(stream)
+            pkv.decode_partitions(out, w.q[L], kc, vc, w.block_table, w.context_lens,
+                                  w.max_context_len, w.softmax_scale, ks[L], vs[L],
+                                  partition_tokens=pt, workspace=work, stream=stream)
+            evs[k][1].record(stream)
+            pkv.combine_partitions(out, w.context_lens, w.max_context_len, w.H_KV,
+                                   w.block_size, partition_tokens=pt, workspace=work,
+                                   stream=stream)
+            k += 1
+    torch.cuda.synchronize()
+    kern_ms = sorted(a.elapsed_time(b) for a, b in evs)
+    kern_avg_ms = sum(kern_ms) / len(kern_ms)
+
+    att = metrics.attention_bytes(lens, w.H_Q, w.H_KV, w.d_h, w.block_size, w.kv_dtype,
+                                  w.q_dtype)
+    app = metrics.append_bytes(w.B, w.H_KV, w.d_h, w.kv_dtype, w.q_dtype)
+    step_bytes = w.layers * (att["total"] + app)
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    achieved = att["total"] / (kern_avg_ms * 1e-3) / 1e9
+    traffic = measured_traffic(args.workload, pt)
+    log(f"partition={pt} parts={parts} workspace={ws_bytes} B; step {ms_per_step * 1e3:.1f} us "
+        f"({ms_per_step * 1e3 / w.layers:.1f} us/layer); partition kernel avg "
+        f"{kern_avg_ms * 1e3:.1f} us (p10 {kern_ms[len(kern_ms) // 10] * 1e3:.1f}, p90 "
+        f"{kern_ms[9 * len(kern_ms) // 10] * 1e3:.1f}); KV bytes/layer {att['kv']}; "
+        f"kernel {achieved:.0f} GB/s = {100 * achieved / PEAK_GBS:.1f}% of peak")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, (w.q[0], w.k_new[0], w.v_new[0], w.k_cache[0], w.v_cache[0],
+                               ks[0], vs[0]), args.cpu_budget)
+        log(f"cpu oracle: {cpu}")
+
+    res = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.kv_dtype,
+        "data": "synthetic",
+        "config": {"workload": args.workload, "B": w.B, "H_Q": w.H_Q, "H_KV": w.H_KV,
+                   "d_h": w.d_h, "block_size": w.block_size, "kv_dtype": w.kv_dtype,
+                   "q_dtype": w.q_dtype, "layers": w.layers, "partition_tokens": pt,
+                   "partitions_max": parts, "pool_copies": R,
+                   "mean_context": round(sum(lens) / len(lens), 1),
+                   "us_per_step_per_layer": round(ms_per_step * 1e3 / w.layers, 2),
+                   "pct_of_peak_step": round(100 * value / PEAK_GBS, 2)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / PEAK_GBS, 4),
+                     "traffic": traffic,
+                     "kernel": "decode_mfma_kernel" if args.variant != 1 else "decode_generic_kernel",
+                     "algorithmic_bytes_per_launch": att["total"],
+                     "avg_launch_us": round(kern_avg_ms * 1e3, 3)},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

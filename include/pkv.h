@@ -1,0 +1,228 @@
+/*
+ * pkv.h -- C ABI of the paged KV-cache decode library (MI355X / gfx950).
+ *
+ * One decode step for one layer: append each request's new key and value
+ * to its slot, then let each query head attend over every cached position of
+ * its request, reading the cache through a block table.  All terms follow
+ * page 1, "KV cache: Generation state, latency, and allocation":
+ *
+ *   - K, V of one layer are B x H_KV x T x d_h (section 21.1, Eq. 21.1);
+ *     here T is spread over fixed-size blocks of `block_size` slots;
+ *   - H_Q must be divisible by H_KV; query head hq reads KV head hq / g,
+ *     g = H_Q / H_KV, and keeps its own scores (section 21.1);
+ *   - position t of a request lives in logical block t / block_size, slot
+ *     t % block_size; the block table maps the logical block to a physical
+ *     block of the pool (section 21.5, Table 21.1);
+ *   - the new token's K and V are appended first and the query reads them
+ *     too (section 21.1; section 21.6, Eq. 21.6), so `context_lens` counts
+ *     positions AFTER the append;
+ *   - blocks come from a pool with a free queue and reference counts, and a
+ *     block returns to the pool when its last reference goes (section
+ *     21.5, steps 2-5; page 2 "KV Cache Explained", section "Why
+ *     PagedAttention allocates KV in blocks").
+ *
+ * Memory layout (device, caller-owned):
+ *   k_cache, v_cache : [num_blocks][H_KV][block_size][d_h] of kv_dtype,
+ *                      separate K and V arrays per layer
+ *   k_scale, v_scale : [num_blocks][H_KV] float, fp8 only (stored value =
+ *                      E4M3 code value * scale), NULL otherwise
+ *   block_table      : [B][max_blocks_per_seq] int32, row-major; entries
+ *                      past a request's last block are never read
+ *   context_lens     : [B] int32, positions after the append, >= 1
+ *   q                : [B][H_Q][d_h] of q_dtype
+ *   k_new, v_new     : [B][H_KV][d_h] of q_dtype
+ *   out              : [B][H_Q][d_h] float
+ *
+ * Conventions:
+ *   - every function returns a pkv_status; nothing throws across the ABI;
+ *   - device functions are asynchronous on `stream` (a hipStream_t, NULL =
+ *     the default stream); argument checks happen on the host before any
+ *     launch, and a failed check launches nothing;
+ *   - the library never allocates device memory: the caller passes every
+ *     device buffer, including the attention workspace;
+ *   - device-side values are trusted to be in range; a block id outside
+ *     [0, num_blocks) or a context length outside [1, max_blocks_per_seq *
+ *     block_size] is clamped (attention) or skipped (append) so that no
+ *     access leaves the caller's buffers, and the results for that request
+ *     are unspecified;
+ *   - the pool is host-only, never touches device memory and is not
+ *     thread-safe: callers serialise access to one pool.
+ */
+#ifndef PKV_H
+#define PKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PKV_OK = 0,
+  PKV_ERR_INVALID_ARG = -1,   /* bad shape, pointer, dtype or size          */
+  PKV_ERR_OUT_OF_BLOCKS = -2, /* pool has no free block                     */
+  PKV_ERR_BAD_BLOCK = -3,     /* block id not live (free or out of range)   */
+  PKV_ERR_SHARED_BLOCK = -4,  /* write into a block whose refcount > 1      */
+  PKV_ERR_HIP = -5,           /* a HIP launch or runtime call failed        */
+  PKV_ERR_WORKSPACE = -6,     /* workspace missing or too small             */
+  PKV_ERR_UNSUPPORTED = -7    /* valid but not implemented (dtype pair ...) */
+} pkv_status;
+
+typedef enum { PKV_F32 = 0, PKV_BF16 = 1, PKV_FP8_E4M3 = 2 } pkv_dtype;
+
+typedef void* pkv_stream_t; /* hipStream_t */
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* pkv_status_string(int status);
+
+/* ABI version of this header (bumped on incompatible change). */
+int pkv_abi_version(void);
+
+/* ------------------------------------------------------------------------
+ * Host block pool (page 1 section 21.5 Table 21.1 and steps 1-5; page 2
+ * "Why PagedAttention allocates KV in blocks"; page 3 "xf_kv_cache",
+ * "End-to-end flow": private blocks return to the free list, shared ones
+ * only lose a reference).
+ *
+ * The free pool is a FIFO queue: alloc pops the head, a block whose count
+ * drops to zero is pushed to the tail.  All functions leave the pool
+ * unchanged when they return an error.
+ * ---------------------------------------------------------------------- */
+typedef struct pkv_pool pkv_pool;
+
+/* Create a pool of `num_blocks` blocks of `block_size` slots.  `free_order`
+ * (nullable) is the initial queue order and must be a permutation of
+ * 0..num_blocks-1; NULL means 0, 1, 2, ...  *out receives a handle owned by
+ * the library (free it with pkv_pool_destroy).  INVALID_ARG on bad sizes or
+ * a non-permutation. */
+int pkv_pool_create(int32_t num_blocks, int32_t block_size, const int32_t* free_order,
+                    pkv_pool** out);
+void pkv_pool_destroy(pkv_pool* pool);
+
+/* Pop the queue head, set its refcount to 1.  OUT_OF_BLOCKS if empty. */
+int pkv_pool_alloc(pkv_pool* pool, int32_t* block_id);
+/* Map a live block into one more table (section 21.5 step 3).  BAD_BLOCK
+ * if the block is free or out of range. */
+int pkv_pool_incref(pkv_pool* pool, int32_t block_id);
+/* Drop one reference; at zero the block goes to the queue tail (step 4).
+ * BAD_BLOCK if the block is free or out of range. */
+int pkv_pool_decref(pkv_pool* pool, int32_t block_id);
+int pkv_pool_refcount(const pkv_pool* pool, int32_t block_id, int32_t* out);
+int pkv_pool_num_free(const pkv_pool* pool, int32_t* out);
+int pkv_pool_num_used(const pkv_pool* pool, int32_t* out);
+/* Copy the current free queue, head first, into `ids` (capacity `cap`);
+ * *count receives the queue length.  INVALID_ARG if cap is too small. */
+int pkv_pool_free_queue(const pkv_pool* pool, int32_t* ids, int32_t cap, int32_t* count);
+
+/* Make room for zero-based position `ctx_before` of one request whose host
+ * table row holds *n_blocks entries (capacity max_blocks).  Takes a new
+ * block iff ctx_before % block_size == 0 (section 21.5 step 2) and then
+ * increments *n_blocks.  Returns the target physical block and slot in
+ * *block_out / *slot_out.  INVALID_ARG if *n_blocks does not match
+ * ctx_before or the row is full; OUT_OF_BLOCKS if no block is free;
+ * SHARED_BLOCK if the target block has refcount > 1 (copy-on-write,
+ * section 21.5, is not done by this call). */
+int pkv_seq_prepare_append(pkv_pool* pool, int32_t* table_row, int32_t max_blocks,
+                           int32_t ctx_before, int32_t* n_blocks, int32_t* block_out,
+                           int32_t* slot_out);
+/* Map the first n_full_blocks blocks of src_row into dst_row, one more
+ * reference each (section 21.5 step 3).  BAD_BLOCK if any is not live. */
+int pkv_seq_share_prefix(pkv_pool* pool, const int32_t* src_row, int32_t n_full_blocks,
+                         int32_t* dst_row);
+/* Drop one reference to each of the n_blocks blocks (steps 4-5).  Checks
+ * all ids first; BAD_BLOCK (and no change) if any is not live, or if a
+ * block appears more often than it has references. */
+int pkv_seq_release(pkv_pool* pool, const int32_t* table_row, int32_t n_blocks);
+
+/* ------------------------------------------------------------------------
+ * Device entry points
+ * ---------------------------------------------------------------------- */
+
+/* Append (page 1 section 21.6, Eq. 21.6; slot rule of section 21.5).
+ * For every request b: t = context_lens[b] - 1, p = block_table[b][t /
+ * block_size], r = t % block_size, and for every KV head h
+ *   k_cache[p][h][r][:] = store(k_new[b][h][:]),  same for V.
+ * store is a bit copy when in_dtype == kv_dtype (F32 or BF16), and for
+ * kv_dtype FP8_E4M3 the OCP E4M3 code of fp32(x) / scale[p][h] rounded to
+ * nearest even and saturated to +-448 (NaN stays NaN).  Supported
+ * (in_dtype, kv_dtype): (F32, F32), (BF16, BF16), (BF16, FP8_E4M3),
+ * (F32, FP8_E4M3).  Every other pool byte is left untouched.  Requests
+ * whose slot is not writable (length or block id out of range) are
+ * skipped.  Requests must not share the written block. */
+int pkv_kv_append(const void* k_new, const void* v_new, int in_dtype, void* k_cache,
+                  void* v_cache, int kv_dtype, const float* k_scale, const float* v_scale,
+                  const int32_t* block_table, int32_t max_blocks_per_seq,
+                  const int32_t* context_lens, int32_t B, int32_t H_KV, int32_t d_h,
+                  int32_t block_size, int32_t num_blocks, pkv_stream_t stream);
+
+/* Partition (split-K) planning for paged_decode_attention.  Each request's
+ * positions are cut into partitions of `partition_tokens` positions (a
+ * multiple of block_size; 0 picks the library default for this shape).
+ * *partition_tokens_out receives the value used, *max_partitions_out =
+ * ceil(max_context_len / partition_tokens), and *workspace_bytes the
+ * device workspace paged_decode_attention needs (0 when every request fits
+ * one partition). */
+int pkv_decode_plan(int32_t B, int32_t H_Q, int32_t H_KV, int32_t d_h, int32_t block_size,
+                    int32_t max_context_len, int32_t partition_tokens,
+                    int32_t* partition_tokens_out, int32_t* max_partitions_out,
+                    size_t* workspace_bytes);
+
+/* Paged decode attention (page 1 section 21.1: every query head normalises
+ * its scores over the request's cached keys, its own new key included, and
+ * mixes the values; section 21.5: attention follows the block table).  For
+ * request b, query head hq, KV head h = hq / (H_Q / H_KV), n = context_lens[b]:
+ *   s_t = softmax_scale * q[b][hq] . K_t   for t < n  (K_t read at the
+ *         table's block and slot; fp8 values are code * k_scale[p][h])
+ *   out[b][hq][:] = sum_t exp(s_t - max s) V_t / sum_t exp(s_t - max s)
+ * computed in fp32.  Slots at positions >= n are never read as keys or
+ * values (they may hold anything, NaN included).  `max_context_len` (a host
+ * value) must be >= every context_lens[b]; it sizes the grid.  Supported
+ * (q_dtype, kv_dtype): (F32, F32), (BF16, BF16), (BF16, FP8_E4M3).
+ * `workspace` holds per-partition partial results when a request spans
+ * more than one partition; its size comes from pkv_decode_plan (WORKSPACE
+ * if too small).  Launches the partition kernel and, when any request can
+ * span more than one partition, the combine kernel. */
+int pkv_paged_decode_attention(float* out, const void* q, int q_dtype, const void* k_cache,
+                               const void* v_cache, int kv_dtype, const float* k_scale,
+                               const float* v_scale, const int32_t* block_table,
+                               int32_t max_blocks_per_seq, const int32_t* context_lens,
+                               int32_t max_context_len, int32_t B, int32_t H_Q, int32_t H_KV,
+                               int32_t d_h, int32_t block_size, int32_t num_blocks,
+                               float softmax_scale, int32_t partition_tokens, void* workspace,
+                               size_t workspace_bytes, pkv_stream_t stream);
+
+/* The two launches of pkv_paged_decode_attention, callable separately (for
+ * timing each kernel).  decode_partitions runs the per-partition online
+ * softmax (same arguments); it writes `out` directly for requests that fit
+ * one partition and partial (max, sum, unnormalised output) triples to the
+ * workspace otherwise.  combine_partitions merges those partials with the
+ * log-sum-exp rule: M = max_p m_p, out = sum_p o_p e^(m_p - M) /
+ * sum_p l_p e^(m_p - M).  Call it with the same B, H_Q, d_h, block size,
+ * partition and max_context_len as decode_partitions. */
+int pkv_decode_partitions(float* out, const void* q, int q_dtype, const void* k_cache,
+                          const void* v_cache, int kv_dtype, const float* k_scale,
+                          const float* v_scale, const int32_t* block_table,
+                          int32_t max_blocks_per_seq, const int32_t* context_lens,
+                          int32_t max_context_len, int32_t B, int32_t H_Q, int32_t H_KV,
+                          int32_t d_h, int32_t block_size, int32_t num_blocks,
+                          float softmax_scale, int32_t partition_tokens, void* workspace,
+                          size_t workspace_bytes, pkv_stream_t stream);
+int pkv_combine_partitions(float* out, const int32_t* context_lens, int32_t max_context_len,
+                           int32_t B, int32_t H_Q, int32_t H_KV, int32_t d_h,
+                           int32_t block_size, int32_t partition_tokens, const void* workspace,
+                           size_t workspace_bytes, pkv_stream_t stream);
+
+/* Kernel selection for the attention calls (process-wide, not
+ * thread-safe).  AUTO uses the MFMA kernel where it applies (d_h = 128,
+ * block_size = 16, BF16 query with BF16 or FP8 cache, H_Q / H_KV <= 32) and
+ * the generic VALU kernel otherwise; GENERIC and MFMA force one (MFMA
+ * returns UNSUPPORTED outside its shapes).  Returns the previous value. */
+typedef enum { PKV_VARIANT_AUTO = 0, PKV_VARIANT_GENERIC = 1, PKV_VARIANT_MFMA = 2 } pkv_variant;
+int pkv_set_decode_variant(int variant);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKV_H */

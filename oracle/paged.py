@@ -55,14 +55,15 @@ def slot_of(block_table_row, position: int, block_size: int) -> tuple:
 
 def append(k_cache, v_cache, kv_dtype: str, k_new, v_new, in_dtype: str,
            block_table, context_lens, block_size: int,
-           k_scale=None, v_scale=None):
-    """Write each request's new K, V into slot (n_b - 1); return new pools.
+           k_scale=None, v_scale=None, inplace=False):
+    """Write each request's new K, V into slot (n_b - 1); return the pools
+    (new copies unless ``inplace``).
 
     Stored form: the same bits for f32 -> f32 and bf16 -> bf16; for fp8, the
     E4M3FN code of fp32(x) / scale[p, h] (see ``codecs``).  Every other pool
     byte is left untouched."""
-    kc = np.array(k_cache, copy=True)
-    vc = np.array(v_cache, copy=True)
+    kc = k_cache if inplace else np.array(k_cache, copy=True)
+    vc = v_cache if inplace else np.array(v_cache, copy=True)
     num_blocks = kc.shape[0]
     B, H_KV, _ = np.shape(k_new)
     for b in range(B):
@@ -144,12 +145,12 @@ def attend(q, q_dtype: str, k_cache, v_cache, kv_dtype: str, block_table,
 
 def decode_step(q, q_dtype, k_new, v_new, k_cache, v_cache, kv_dtype,
                 block_table, context_lens, block_size, softmax_scale,
-                k_scale=None, v_scale=None, requests=None):
+                k_scale=None, v_scale=None, requests=None, inplace=False):
     """Append, then attend (page 1, section 21.1 and Eq. 21.6).
 
     Returns (k_cache_after, v_cache_after, out)."""
     kc, vc = append(k_cache, v_cache, kv_dtype, k_new, v_new, q_dtype,
-                    block_table, context_lens, block_size, k_scale, v_scale)
+                    block_table, context_lens, block_size, k_scale, v_scale, inplace)
     out = attend(q, q_dtype, kc, vc, kv_dtype, block_table, context_lens,
                  block_size, softmax_scale, k_scale, v_scale, requests)
     return kc, vc, out

@@ -1,0 +1,194 @@
+"""Paged KV-cache decode attention for MI355X (gfx950).
+
+A thin Python layer over the C ABI of ``libpkv.so`` (include/pkv.h).  The
+functions below only read shapes and raw pointers off torch tensors and pass
+them on with the current HIP stream; all work runs in the library's HIP
+kernels and host pool.  Importing the package does not load the library;
+the first call does, and fails loudly if it has not been built.
+"""
+
+from __future__ import annotations
+
+import ctypes as C
+
+from . import _lib
+from ._lib import (PKV_BF16, PKV_F32, PKV_FP8_E4M3, PKV_VARIANT_AUTO, PKV_VARIANT_GENERIC,
+                   PKV_VARIANT_MFMA, PkvError, check, load)
+
+__all__ = ["kv_append", "decode_plan", "paged_decode_attention", "decode_partitions",
+           "combine_partitions", "set_decode_variant", "BlockPool", "PkvError", "load",
+           "PKV_F32", "PKV_BF16", "PKV_FP8_E4M3", "PKV_VARIANT_AUTO", "PKV_VARIANT_GENERIC",
+           "PKV_VARIANT_MFMA"]
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.float32:
+        return PKV_F32
+    if t.dtype == torch.bfloat16:
+        return PKV_BF16
+    if t.dtype in (torch.float8_e4m3fn, torch.uint8):
+        return PKV_FP8_E4M3
+    raise TypeError(f"unsupported tensor dtype {t.dtype}")
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to the library must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is not None:
+        return stream if isinstance(stream, int) else stream.cuda_stream
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+def kv_append(k_new, v_new, k_cache, v_cache, block_table, context_lens,
+              k_scale=None, v_scale=None, stream=None):
+    """pkv_kv_append: write k_new/v_new [B, H_KV, d_h] into slot
+    context_lens[b] - 1 of each request (lengths after the append)."""
+    B, H_KV, d_h = k_new.shape
+    num_blocks, _, bs, _ = k_cache.shape
+    check(load().pkv_kv_append(_ptr(k_new), _ptr(v_new), _dtype_code(k_new), _ptr(k_cache),
+                               _ptr(v_cache), _dtype_code(k_cache), _ptr(k_scale),
+                               _ptr(v_scale), _ptr(block_table), block_table.shape[1],
+                               _ptr(context_lens), B, H_KV, d_h, bs, num_blocks,
+                               _stream(stream)), "pkv_kv_append")
+
+
+def decode_plan(B, H_Q, H_KV, d_h, block_size, max_context_len, partition_tokens=0):
+    """pkv_decode_plan -> (partition_tokens, max_partitions, workspace_bytes)."""
+    pt, parts, ws = C.c_int32(), C.c_int32(), C.c_size_t()
+    check(load().pkv_decode_plan(B, H_Q, H_KV, d_h, block_size, max_context_len,
+                                 partition_tokens, C.byref(pt), C.byref(parts), C.byref(ws)),
+          "pkv_decode_plan")
+    return pt.value, parts.value, ws.value
+
+
+def _attn_args(out, q, k_cache, v_cache, block_table, context_lens, max_context_len,
+               softmax_scale, k_scale, v_scale, partition_tokens, workspace, stream):
+    B, H_Q, d_h = q.shape
+    num_blocks, H_KV, bs, _ = k_cache.shape
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    return (_ptr(out), _ptr(q), _dtype_code(q), _ptr(k_cache), _ptr(v_cache),
+            _dtype_code(k_cache), _ptr(k_scale), _ptr(v_scale), _ptr(block_table),
+            block_table.shape[1], _ptr(context_lens), int(max_context_len), B, H_Q, H_KV, d_h,
+            bs, num_blocks, float(softmax_scale), int(partition_tokens), _ptr(workspace),
+            ws_bytes, _stream(stream))
+
+
+def paged_decode_attention(out, q, k_cache, v_cache, block_table, context_lens,
+                           max_context_len, softmax_scale, k_scale=None, v_scale=None,
+                           partition_tokens=0, workspace=None, stream=None):
+    """pkv_paged_decode_attention: out [B, H_Q, d_h] fp32."""
+    check(load().pkv_paged_decode_attention(*_attn_args(
+        out, q, k_cache, v_cache, block_table, context_lens, max_context_len, softmax_scale,
+        k_scale, v_scale, partition_tokens, workspace, stream)), "pkv_paged_decode_attention")
+
+
+def decode_partitions(out, q, k_cache, v_cache, block_table, context_lens, max_context_len,
+                      softmax_scale, k_scale=None, v_scale=None, partition_tokens=0,
+                      workspace=None, stream=None):
+    """pkv_decode_partitions: the partition kernel alone."""
+    check(load().pkv_decode_partitions(*_attn_args(
+        out, q, k_cache, v_cache, block_table, context_lens, max_context_len, softmax_scale,
+        k_scale, v_scale, partition_tokens, workspace, stream)), "pkv_decode_partitions")
+
+
+def combine_partitions(out, context_lens, max_context_len, H_KV, block_size,
+                       partition_tokens=0, workspace=None, stream=None):
+    """pkv_combine_partitions: the split-K combine kernel alone."""
+    B, H_Q, d_h = out.shape
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    check(load().pkv_combine_partitions(_ptr(out), _ptr(context_lens), int(max_context_len), B,
+                                        H_Q, H_KV, d_h, block_size, int(partition_tokens),
+                                        _ptr(workspace), ws_bytes, _stream(stream)),
+          "pkv_combine_partitions")
+
+
+def set_decode_variant(variant: int) -> int:
+    """pkv_set_decode_variant; returns the previous value."""
+    return load().pkv_set_decode_variant(int(variant))
+
+
+class BlockPool:
+    """The library's host block pool (pkv_pool_*, pkv_seq_*)."""
+
+    def __init__(self, num_blocks: int, block_size: int, free_order=None):
+        lib = load()
+        h = C.c_void_p()
+        arr = None
+        if free_order is not None:
+            free_order = [int(x) for x in free_order]
+            arr = (C.c_int32 * len(free_order))(*free_order)
+            if len(free_order) != num_blocks:
+                raise PkvError(-1, "pkv_pool_create")
+        check(lib.pkv_pool_create(num_blocks, block_size, arr, C.byref(h)), "pkv_pool_create")
+        self._h = h
+        self._lib = lib
+        self.num_blocks = num_blocks
+        self.block_size = block_size
+
+    def close(self):
+        if self._h:
+            self._lib.pkv_pool_destroy(self._h)
+            self._h = C.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def alloc(self) -> int:
+        b = C.c_int32()
+        check(self._lib.pkv_pool_alloc(self._h, C.byref(b)), "pkv_pool_alloc")
+        return b.value
+
+    def incref(self, block: int):
+        check(self._lib.pkv_pool_incref(self._h, block), "pkv_pool_incref")
+
+    def decref(self, block: int):
+        check(self._lib.pkv_pool_decref(self._h, block), "pkv_pool_decref")
+
+    def refcount(self, block: int) -> int:
+        r = C.c_int32()
+        check(self._lib.pkv_pool_refcount(self._h, block, C.byref(r)), "pkv_pool_refcount")
+        return r.value
+
+    def num_free(self) -> int:
+        r = C.c_int32()
+        check(self._lib.pkv_pool_num_free(self._h, C.byref(r)), "pkv_pool_num_free")
+        return r.value
+
+    def num_used(self) -> int:
+        r = C.c_int32()
+        check(self._lib.pkv_pool_num_used(self._h, C.byref(r)), "pkv_pool_num_used")
+        return r.value
+
+    def free_queue(self) -> list:
+        n = C.c_int32()
+        buf = (C.c_int32 * max(1, self.num_blocks))()
+        check(self._lib.pkv_pool_free_queue(self._h, buf, self.num_blocks, C.byref(n)),
+              "pkv_pool_free_queue")
+        return list(buf[:n.value])
+
+    def prepare_append(self, row, n_blocks: int, ctx_before: int):
+        """row: a ctypes int32 array (the host table row, updated in place).
+        Returns (n_blocks_after, block, slot)."""
+        nb, blk, slot = C.c_int32(n_blocks), C.c_int32(), C.c_int32()
+        check(self._lib.pkv_seq_prepare_append(self._h, row, len(row), ctx_before,
+                                               C.byref(nb), C.byref(blk), C.byref(slot)),
+              "pkv_seq_prepare_append")
+        return nb.value, blk.value, slot.value
+
+    def share_prefix(self, src_row, n_full_blocks: int, dst_row):
+        check(self._lib.pkv_seq_share_prefix(self._h, src_row, n_full_blocks, dst_row),
+              "pkv_seq_share_prefix")
+
+    def release(self, row, n_blocks: int):
+        check(self._lib.pkv_seq_release(self._h, row, n_blocks), "pkv_seq_release")

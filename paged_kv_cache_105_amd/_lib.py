@@ -1,0 +1,89 @@
+"""ctypes declarations of the C ABI in include/pkv.h (marshalling only).
+
+Every function of the header is declared here with the same name and
+argument order.  Loading fails loudly when libpkv.so has not been built:
+there is no fallback implementation.
+"""
+
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libpkv.so")
+
+PKV_OK = 0
+STATUS_NAMES = {0: "ok", -1: "invalid_arg", -2: "out_of_blocks", -3: "bad_block",
+                -4: "shared_block", -5: "hip", -6: "workspace", -7: "unsupported"}
+PKV_F32, PKV_BF16, PKV_FP8_E4M3 = 0, 1, 2
+PKV_VARIANT_AUTO, PKV_VARIANT_GENERIC, PKV_VARIANT_MFMA = 0, 1, 2
+
+_i32 = C.c_int32
+_pi32 = C.POINTER(C.c_int32)
+_vp = C.c_void_p
+_sz = C.c_size_t
+_f = C.c_float
+
+# name -> (restype, argtypes), in header order
+SIGNATURES = {
+    "pkv_status_string": (C.c_char_p, [C.c_int]),
+    "pkv_abi_version": (C.c_int, []),
+    "pkv_pool_create": (C.c_int, [_i32, _i32, _pi32, C.POINTER(_vp)]),
+    "pkv_pool_destroy": (None, [_vp]),
+    "pkv_pool_alloc": (C.c_int, [_vp, _pi32]),
+    "pkv_pool_incref": (C.c_int, [_vp, _i32]),
+    "pkv_pool_decref": (C.c_int, [_vp, _i32]),
+    "pkv_pool_refcount": (C.c_int, [_vp, _i32, _pi32]),
+    "pkv_pool_num_free": (C.c_int, [_vp, _pi32]),
+    "pkv_pool_num_used": (C.c_int, [_vp, _pi32]),
+    "pkv_pool_free_queue": (C.c_int, [_vp, _pi32, _i32, _pi32]),
+    "pkv_seq_prepare_append": (C.c_int, [_vp, _pi32, _i32, _i32, _pi32, _pi32, _pi32]),
+    "pkv_seq_share_prefix": (C.c_int, [_vp, _pi32, _i32, _pi32]),
+    "pkv_seq_release": (C.c_int, [_vp, _pi32, _i32]),
+    "pkv_kv_append": (C.c_int, [_vp, _vp, C.c_int, _vp, _vp, C.c_int, _vp, _vp, _vp, _i32, _vp,
+                                _i32, _i32, _i32, _i32, _i32, _vp]),
+    "pkv_decode_plan": (C.c_int, [_i32, _i32, _i32, _i32, _i32, _i32, _i32, _pi32, _pi32,
+                                  C.POINTER(_sz)]),
+    "pkv_paged_decode_attention": (C.c_int, [_vp, _vp, C.c_int, _vp, _vp, C.c_int, _vp, _vp,
+                                             _vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
+                                             _i32, _f, _i32, _vp, _sz, _vp]),
+    "pkv_decode_partitions": (C.c_int, [_vp, _vp, C.c_int, _vp, _vp, C.c_int, _vp, _vp, _vp,
+                                        _i32, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f,
+                                        _i32, _vp, _sz, _vp]),
+    "pkv_combine_partitions": (C.c_int, [_vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
+                                         _vp, _sz, _vp]),
+    "pkv_set_decode_variant": (C.c_int, [C.c_int]),
+}
+
+_lib = None
+
+
+class PkvError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        self.name = STATUS_NAMES.get(status, str(status))
+        super().__init__(f"{where}: {self.name} ({status})")
+
+
+def load():
+    """Load libpkv.so once; raise if it is missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            f"{LIB_PATH} is not built; run `python -m paged_kv_cache_105_amd.build` "
+            "(or __graft_entry__.build()) first")
+    lib = C.CDLL(LIB_PATH)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def check(status: int, where: str):
+    if status != PKV_OK:
+        raise PkvError(status, where)

@@ -1,0 +1,287 @@
+// C ABI entry points for the device path: argument checks on the host, the
+// partition plan, and the kernel launches.  See include/pkv.h for the
+// contract of each function.
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdint>
+
+#include "pkv.h"
+#include "pkv_device.h"
+
+namespace pkv {
+hipError_t launch_kv_append(int in_dtype, int kv_dtype, const void* k_new, const void* v_new,
+                            void* k_cache, void* v_cache, const float* k_scale,
+                            const float* v_scale, const int32_t* block_table,
+                            int max_blocks_per_seq, const int32_t* context_lens, int B, int H_KV,
+                            int d_h, int block_size, int num_blocks, hipStream_t stream);
+hipError_t launch_decode_generic(int q_dtype, int kv_dtype, const DecodeArgs& a,
+                                 hipStream_t stream);
+size_t generic_lds_bytes(int g, int d_h, int partition_tokens);
+bool mfma_supports(int q_dtype, int kv_dtype, int d_h, int block_size, int g,
+                   int partition_tokens);
+hipError_t launch_decode_mfma(int kv_dtype, const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_combine(float* out, const int32_t* context_lens, Workspace ws, int B, int H_Q,
+                          int d_h, int partition_tokens, int max_parts, hipStream_t stream);
+}  // namespace pkv
+
+namespace {
+
+int g_variant = PKV_VARIANT_AUTO;
+
+constexpr int kMaxDh = 256;
+constexpr int kMaxGenericPartition = 256;
+constexpr size_t kMaxGenericLds = 64 * 1024;
+constexpr size_t kAlign = 256;
+
+bool valid_dtype(int d) { return d == PKV_F32 || d == PKV_BF16 || d == PKV_FP8_E4M3; }
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// Default partition length: enough workgroups to cover the chip several
+// times over, but no shorter than 4 blocks and no longer than 256 positions
+// (the longest partition both kernels take).
+int default_partition(int B, int H_KV, int block_size, int max_context_len) {
+  const long long target_groups = 4LL * 256;  // 256 compute units
+  const long long heads = static_cast<long long>(B) * H_KV;
+  int pt = 256;
+  while (pt > 4 * block_size && pt > block_size &&
+         heads * ((max_context_len + pt - 1) / pt) < target_groups)
+    pt /= 2;
+  pt = std::max(block_size, pt / block_size * block_size);
+  return pt;
+}
+
+int resolve_partition(int B, int H_KV, int block_size, int max_context_len, int requested) {
+  if (requested > 0) return requested;
+  return default_partition(B, H_KV, block_size, max_context_len);
+}
+
+struct Plan {
+  int partition_tokens;
+  int max_parts;
+  size_t o_bytes, ml_bytes, total;
+};
+
+int make_plan(int B, int H_Q, int H_KV, int d_h, int block_size, int max_context_len,
+              int partition_tokens, Plan* plan) {
+  if (B < 1 || H_Q < 1 || H_KV < 1 || H_Q % H_KV || d_h < 1 || d_h > kMaxDh || block_size < 1 ||
+      max_context_len < 1 || partition_tokens < 0)
+    return PKV_ERR_INVALID_ARG;
+  const int pt = resolve_partition(B, H_KV, block_size, max_context_len, partition_tokens);
+  if (pt % block_size) return PKV_ERR_INVALID_ARG;
+  plan->partition_tokens = pt;
+  plan->max_parts = (max_context_len + pt - 1) / pt;
+  // grid.x limit of the launch and the combine kernel's LDS weight array (64 KiB)
+  if (plan->max_parts > 16384) return PKV_ERR_INVALID_ARG;
+  if (plan->max_parts == 1) {
+    plan->o_bytes = plan->ml_bytes = plan->total = 0;
+  } else {
+    plan->o_bytes = align_up(sizeof(float) * pkv::ws_o_floats(B, H_Q, plan->max_parts, d_h));
+    plan->ml_bytes = align_up(sizeof(float) * pkv::ws_ml_floats(B, H_Q, plan->max_parts));
+    plan->total = plan->o_bytes + plan->ml_bytes;
+  }
+  return PKV_OK;
+}
+
+int check_attention_args(const float* out, const void* q, int q_dtype, const void* k_cache,
+                         const void* v_cache, int kv_dtype, const float* k_scale,
+                         const float* v_scale, const int32_t* block_table,
+                         int max_blocks_per_seq, const int32_t* context_lens,
+                         int max_context_len, int B, int H_Q, int H_KV, int d_h, int block_size,
+                         int num_blocks, float softmax_scale) {
+  if (!out || !q || !k_cache || !v_cache || !block_table || !context_lens)
+    return PKV_ERR_INVALID_ARG;
+  if (!valid_dtype(q_dtype) || !valid_dtype(kv_dtype) || q_dtype == PKV_FP8_E4M3)
+    return PKV_ERR_INVALID_ARG;
+  if (B < 1 || H_Q < 1 || H_KV < 1 || H_Q % H_KV || d_h < 1 || d_h > kMaxDh || block_size < 1 ||
+      num_blocks < 1 || max_blocks_per_seq < 1 || max_context_len < 1)
+    return PKV_ERR_INVALID_ARG;
+  if (static_cast<long long>(max_context_len) >
+      static_cast<long long>(max_blocks_per_seq) * block_size)
+    return PKV_ERR_INVALID_ARG;
+  if (!std::isfinite(softmax_scale)) return PKV_ERR_INVALID_ARG;
+  if (kv_dtype == PKV_FP8_E4M3 && (!k_scale || !v_scale)) return PKV_ERR_INVALID_ARG;
+  const bool pair_ok = (q_dtype == PKV_F32 && kv_dtype == PKV_F32) ||
+                       (q_dtype == PKV_BF16 && kv_dtype == PKV_BF16) ||
+                       (q_dtype == PKV_BF16 && kv_dtype == PKV_FP8_E4M3);
+  if (!pair_ok) return PKV_ERR_UNSUPPORTED;
+  // 16-byte row alignment is assumed by the vector loads of the MFMA kernel
+  const uintptr_t align_mask = 15;
+  if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k_cache) |
+       reinterpret_cast<uintptr_t>(v_cache) | reinterpret_cast<uintptr_t>(out)) &
+      align_mask)
+    return PKV_ERR_INVALID_ARG;
+  return PKV_OK;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? PKV_OK : PKV_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char* pkv_status_string(int status) {
+  switch (status) {
+    case PKV_OK: return "ok";
+    case PKV_ERR_INVALID_ARG: return "invalid argument";
+    case PKV_ERR_OUT_OF_BLOCKS: return "out of blocks";
+    case PKV_ERR_BAD_BLOCK: return "bad block";
+    case PKV_ERR_SHARED_BLOCK: return "shared block";
+    case PKV_ERR_HIP: return "HIP error";
+    case PKV_ERR_WORKSPACE: return "workspace missing or too small";
+    case PKV_ERR_UNSUPPORTED: return "unsupported";
+    default: return "unknown status";
+  }
+}
+
+int pkv_abi_version(void) { return 1; }
+
+int pkv_set_decode_variant(int variant) {
+  const int prev = g_variant;
+  if (variant == PKV_VARIANT_AUTO || variant == PKV_VARIANT_GENERIC ||
+      variant == PKV_VARIANT_MFMA)
+    g_variant = variant;
+  return prev;
+}
+
+int pkv_kv_append(const void* k_new, const void* v_new, int in_dtype, void* k_cache,
+                  void* v_cache, int kv_dtype, const float* k_scale, const float* v_scale,
+                  const int32_t* block_table, int32_t max_blocks_per_seq,
+                  const int32_t* context_lens, int32_t B, int32_t H_KV, int32_t d_h,
+                  int32_t block_size, int32_t num_blocks, pkv_stream_t stream) {
+  if (!k_new || !v_new || !k_cache || !v_cache || !block_table || !context_lens)
+    return PKV_ERR_INVALID_ARG;
+  if (!valid_dtype(in_dtype) || !valid_dtype(kv_dtype) || in_dtype == PKV_FP8_E4M3)
+    return PKV_ERR_INVALID_ARG;
+  if (B < 1 || H_KV < 1 || d_h < 1 || d_h > kMaxDh || block_size < 1 || num_blocks < 1 ||
+      max_blocks_per_seq < 1)
+    return PKV_ERR_INVALID_ARG;
+  if (kv_dtype == PKV_FP8_E4M3 && (!k_scale || !v_scale)) return PKV_ERR_INVALID_ARG;
+  const bool pair_ok = (in_dtype == kv_dtype) || kv_dtype == PKV_FP8_E4M3;
+  if (!pair_ok) return PKV_ERR_UNSUPPORTED;
+  return hip_status(pkv::launch_kv_append(in_dtype, kv_dtype, k_new, v_new, k_cache, v_cache,
+                                          k_scale, v_scale, block_table, max_blocks_per_seq,
+                                          context_lens, B, H_KV, d_h, block_size, num_blocks,
+                                          static_cast<hipStream_t>(stream)));
+}
+
+int pkv_decode_plan(int32_t B, int32_t H_Q, int32_t H_KV, int32_t d_h, int32_t block_size,
+                    int32_t max_context_len, int32_t partition_tokens,
+                    int32_t* partition_tokens_out, int32_t* max_partitions_out,
+                    size_t* workspace_bytes) {
+  Plan plan;
+  const int st =
+      make_plan(B, H_Q, H_KV, d_h, block_size, max_context_len, partition_tokens, &plan);
+  if (st != PKV_OK) return st;
+  if (partition_tokens_out) *partition_tokens_out = plan.partition_tokens;
+  if (max_partitions_out) *max_partitions_out = plan.max_parts;
+  if (workspace_bytes) *workspace_bytes = plan.total;
+  return PKV_OK;
+}
+
+int pkv_decode_partitions(float* out, const void* q, int q_dtype, const void* k_cache,
+                          const void* v_cache, int kv_dtype, const float* k_scale,
+                          const float* v_scale, const int32_t* block_table,
+                          int32_t max_blocks_per_seq, const int32_t* context_lens,
+                          int32_t max_context_len, int32_t B, int32_t H_Q, int32_t H_KV,
+                          int32_t d_h, int32_t block_size, int32_t num_blocks,
+                          float softmax_scale, int32_t partition_tokens, void* workspace,
+                          size_t workspace_bytes, pkv_stream_t stream) {
+  int st = check_attention_args(out, q, q_dtype, k_cache, v_cache, kv_dtype, k_scale, v_scale,
+                                block_table, max_blocks_per_seq, context_lens, max_context_len,
+                                B, H_Q, H_KV, d_h, block_size, num_blocks, softmax_scale);
+  if (st != PKV_OK) return st;
+  Plan plan;
+  st = make_plan(B, H_Q, H_KV, d_h, block_size, max_context_len, partition_tokens, &plan);
+  if (st != PKV_OK) return st;
+  if (plan.total > 0 && (!workspace || workspace_bytes < plan.total)) return PKV_ERR_WORKSPACE;
+  if (reinterpret_cast<uintptr_t>(workspace) & 15) return PKV_ERR_INVALID_ARG;
+
+  pkv::DecodeArgs a{};
+  a.out = out;
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
+  a.block_table = block_table;
+  a.context_lens = context_lens;
+  a.ws.o = plan.total ? static_cast<float*>(workspace) : nullptr;
+  a.ws.ml = plan.total ? reinterpret_cast<float*>(static_cast<char*>(workspace) + plan.o_bytes)
+                       : nullptr;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.B = B;
+  a.H_Q = H_Q;
+  a.H_KV = H_KV;
+  a.g = H_Q / H_KV;
+  a.d_h = d_h;
+  a.block_size = block_size;
+  a.num_blocks = num_blocks;
+  a.partition_tokens = plan.partition_tokens;
+  a.max_parts = plan.max_parts;
+  a.scale_log2 = softmax_scale * pkv::kLog2e;
+  if (B > 65535 || H_KV > 65535) return PKV_ERR_INVALID_ARG;
+
+  const bool mfma_ok = pkv::mfma_supports(q_dtype, kv_dtype, d_h, block_size, a.g,
+                                          plan.partition_tokens);
+  bool use_mfma = false;
+  if (g_variant == PKV_VARIANT_MFMA) {
+    if (!mfma_ok) return PKV_ERR_UNSUPPORTED;
+    use_mfma = true;
+  } else if (g_variant == PKV_VARIANT_AUTO) {
+    use_mfma = mfma_ok;
+  }
+  hipError_t e;
+  if (use_mfma) {
+    e = pkv::launch_decode_mfma(kv_dtype, a, static_cast<hipStream_t>(stream));
+  } else {
+    if (plan.partition_tokens > kMaxGenericPartition ||
+        pkv::generic_lds_bytes(a.g, d_h, plan.partition_tokens) > kMaxGenericLds)
+      return PKV_ERR_UNSUPPORTED;
+    e = pkv::launch_decode_generic(q_dtype, kv_dtype, a, static_cast<hipStream_t>(stream));
+  }
+  return hip_status(e);
+}
+
+int pkv_combine_partitions(float* out, const int32_t* context_lens, int32_t max_context_len,
+                           int32_t B, int32_t H_Q, int32_t H_KV, int32_t d_h,
+                           int32_t block_size, int32_t partition_tokens, const void* workspace,
+                           size_t workspace_bytes, pkv_stream_t stream) {
+  if (!out || !context_lens) return PKV_ERR_INVALID_ARG;
+  Plan plan;
+  const int st =
+      make_plan(B, H_Q, H_KV, d_h, block_size, max_context_len, partition_tokens, &plan);
+  if (st != PKV_OK) return st;
+  if (plan.max_parts == 1) return PKV_OK;  // nothing to merge
+  if (!workspace || workspace_bytes < plan.total) return PKV_ERR_WORKSPACE;
+  if (B > 65535 || H_Q > 65535) return PKV_ERR_INVALID_ARG;
+  pkv::Workspace ws;
+  ws.o = static_cast<float*>(const_cast<void*>(workspace));
+  ws.ml = reinterpret_cast<float*>(static_cast<char*>(const_cast<void*>(workspace)) + plan.o_bytes);
+  return hip_status(pkv::launch_combine(out, context_lens, ws, B, H_Q, d_h,
+                                        plan.partition_tokens, plan.max_parts,
+                                        static_cast<hipStream_t>(stream)));
+}
+
+int pkv_paged_decode_attention(float* out, const void* q, int q_dtype, const void* k_cache,
+                               const void* v_cache, int kv_dtype, const float* k_scale,
+                               const float* v_scale, const int32_t* block_table,
+                               int32_t max_blocks_per_seq, const int32_t* context_lens,
+                               int32_t max_context_len, int32_t B, int32_t H_Q, int32_t H_KV,
+                               int32_t d_h, int32_t block_size, int32_t num_blocks,
+                               float softmax_scale, int32_t partition_tokens, void* workspace,
+                               size_t workspace_bytes, pkv_stream_t stream) {
+  int st = pkv_decode_partitions(out, q, q_dtype, k_cache, v_cache, kv_dtype, k_scale, v_scale,
+                                 block_table, max_blocks_per_seq, context_lens, max_context_len,
+                                 B, H_Q, H_KV, d_h, block_size, num_blocks, softmax_scale,
+                                 partition_tokens, workspace, workspace_bytes, stream);
+  if (st != PKV_OK) return st;
+  return pkv_combine_partitions(out, context_lens, max_context_len, B, H_Q, H_KV, d_h,
+                                block_size, partition_tokens, workspace, workspace_bytes,
+                                stream);
+}
+
+}  // extern "C"

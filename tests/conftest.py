@@ -8,3 +8,9 @@ if ROOT not in sys.path:
 
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) and the built HIP library")
+
+
+def pytest_runtest_setup(item):
+    # name the case before it touches the GPU, so a fault can be attributed
+    sys.stderr.write(f"START {item.nodeid}\n")
+    sys.stderr.flush()
