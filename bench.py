@@ -76,26 +76,31 @@ def cpu_baseline(w, layer_tensors, budget_s: float):
     d = dict(q=as_numpy(q), kn=as_numpy(kn), vn=as_numpy(vn), kc=as_numpy(kc).copy(),
              vc=as_numpy(vc).copy(), table=as_numpy(w.block_table), lens=as_numpy(w.context_lens),
              ks=None if ks is None else as_numpy(ks), vs=None if vs is None else as_numpy(vs))
+    # whole decode steps (append of the batch, then attention request by
+    # request) until the time budget is spent; a partial last pass counts
+    # only the requests it finished
+    nbytes, passes, reqs = 0, 0, 0
     with threadpool_limits(limits=1):
         t0 = time.perf_counter()
-        paged.append(d["kc"], d["vc"], w.kv_dtype, d["kn"], d["vn"], w.q_dtype, d["table"],
-                     d["lens"], w.block_size, d["ks"], d["vs"], inplace=True)
-        done = []
-        for b in range(w.B):
-            paged.attend(d["q"], w.q_dtype, d["kc"], d["vc"], w.kv_dtype, d["table"], d["lens"],
-                         w.block_size, w.softmax_scale, d["ks"], d["vs"], requests=[b])
-            done.append(b)
-            if time.perf_counter() - t0 > budget_s:
-                break
+        while time.perf_counter() - t0 < budget_s:
+            paged.append(d["kc"], d["vc"], w.kv_dtype, d["kn"], d["vn"], w.q_dtype, d["table"],
+                         d["lens"], w.block_size, d["ks"], d["vs"], inplace=True)
+            nbytes += metrics.append_bytes(w.B, w.H_KV, w.d_h, w.kv_dtype, w.q_dtype)
+            for b in range(w.B):
+                paged.attend(d["q"], w.q_dtype, d["kc"], d["vc"], w.kv_dtype, d["table"],
+                             d["lens"], w.block_size, w.softmax_scale, d["ks"], d["vs"],
+                             requests=[b])
+                nbytes += metrics.attention_bytes([int(d["lens"][b])], w.H_Q, w.H_KV, w.d_h,
+                                                  w.block_size, w.kv_dtype, w.q_dtype)["total"]
+                reqs += 1
+                if time.perf_counter() - t0 > budget_s:
+                    break
+            passes += 1
         dt = time.perf_counter() - t0
-    lens = [int(d["lens"][b]) for b in done]
-    nbytes = metrics.append_bytes(w.B, w.H_KV, w.d_h, w.kv_dtype, w.q_dtype) + \
-        metrics.attention_bytes(lens, w.H_Q, w.H_KV, w.d_h, w.block_size, w.kv_dtype,
-                                w.q_dtype)["total"]
     return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"one layer: append of all {w.B} requests + attention of {len(done)} of "
-                      f"{w.B} requests ({sum(lens)} positions), float64 numpy, BLAS pinned to "
-                      f"1 thread, {dt:.1f} s"}
+            "sample": f"one layer of this workload: {passes} decode step(s) (append of all "
+                      f"{w.B} requests, attention of {reqs} request-steps), float64 numpy, "
+                      f"BLAS pinned to 1 thread, {dt:.1f} s"}
 
 
 def main():
@@ -109,6 +114,9 @@ def main():
     ap.add_argument("--variant", type=int, default=0, help="0 auto, 1 generic, 2 mfma")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="after the bench, copy a MIB-sized buffer 5 times (plain copy kernel "
+                         "of known size, to scale HBM counters)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -209,6 +217,35 @@ def main():
         f"{kern_ms[9 * len(kern_ms) // 10] * 1e3:.1f}); KV bytes/layer {att['kv']}; "
         f"kernel {achieved:.0f} GB/s = {100 * achieved / PEAK_GBS:.1f}% of peak")
 
+    # reference bandwidths of plain torch kernels on this machine (context for the
+    # % of peak): a 1 GiB device-to-device copy and a 2 GiB read-only sum
+    ref = {}
+    x = torch.empty(2 ** 30 // 2, dtype=torch.bfloat16, device=dev).fill_(1.0)
+    y = torch.empty_like(x[: 2 ** 29 // 2])
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for kind in ("copy", "read"):
+        for rep in range(4):
+            e0.record(stream)
+            if kind == "copy":
+                y.copy_(x[: y.numel()])
+            else:
+                x.sum(dtype=torch.float32)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1)
+        nbytes = 2 * y.numel() * 2 if kind == "copy" else x.numel() * 2
+        ref[f"{kind}_gbs"] = round(nbytes / (ms * 1e-3) / 1e9, 1)
+    del x, y
+    log(f"reference torch kernels: {ref}")
+
+    if args.calibrate_copy > 0:
+        src = torch.ones(args.calibrate_copy * 2 ** 20 // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"calibration copy: {args.calibrate_copy} MiB read + written, 5 launches")
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(w, (w.q[0], w.k_new[0], w.v_new[0], w.k_cache[0], w.v_cache[0],
@@ -234,7 +271,8 @@ def main():
                    "partitions_max": parts, "pool_copies": R,
                    "mean_context": round(sum(lens) / len(lens), 1),
                    "us_per_step_per_layer": round(ms_per_step * 1e3 / w.layers, 2),
-                   "pct_of_peak_step": round(100 * value / PEAK_GBS, 2)},
+                   "pct_of_peak_step": round(100 * value / PEAK_GBS, 2),
+                   "reference_torch_gbs": ref},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / PEAK_GBS, 4),
                      "traffic": traffic,

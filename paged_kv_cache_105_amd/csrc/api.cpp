@@ -7,6 +7,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstdint>
+#include <cstdlib>
 
 #include "pkv.h"
 #include "pkv_device.h"
@@ -22,7 +23,7 @@ hipError_t launch_decode_generic(int q_dtype, int kv_dtype, const DecodeArgs& a,
 size_t generic_lds_bytes(int g, int d_h, int partition_tokens);
 bool mfma_supports(int q_dtype, int kv_dtype, int d_h, int block_size, int g,
                    int partition_tokens);
-hipError_t launch_decode_mfma(int kv_dtype, const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_decode_mfma(int kv_dtype, int depth, const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_combine(float* out, const int32_t* context_lens, Workspace ws, int B, int H_Q,
                           int d_h, int partition_tokens, int max_parts, hipStream_t stream);
 }  // namespace pkv
@@ -30,6 +31,17 @@ hipError_t launch_combine(float* out, const int32_t* context_lens, Workspace ws,
 namespace {
 
 int g_variant = PKV_VARIANT_AUTO;
+
+// Blocks the MFMA kernel keeps in flight ahead of the one it processes.
+// PKV_DECODE_DEPTH (1..3) overrides the default, for tuning measurements.
+int prefetch_depth() {
+  static const int depth = [] {
+    const char* e = std::getenv("PKV_DECODE_DEPTH");
+    const int d = e ? std::atoi(e) : 1;
+    return (d >= 1 && d <= 3) ? d : 1;
+  }();
+  return depth;
+}
 
 constexpr int kMaxDh = 256;
 constexpr int kMaxGenericPartition = 256;
@@ -236,7 +248,7 @@ int pkv_decode_partitions(float* out, const void* q, int q_dtype, const void* k_
   }
   hipError_t e;
   if (use_mfma) {
-    e = pkv::launch_decode_mfma(kv_dtype, a, static_cast<hipStream_t>(stream));
+    e = pkv::launch_decode_mfma(kv_dtype, prefetch_depth(), a, static_cast<hipStream_t>(stream));
   } else {
     if (plan.partition_tokens > kMaxGenericPartition ||
         pkv::generic_lds_bytes(a.g, d_h, plan.partition_tokens) > kMaxGenericLds)

@@ -72,6 +72,7 @@ struct Raw<DT_BF16> {
 template <>
 struct Raw<DT_FP8> {
   u32x2 w[4];
+  float scale;  // the block's scale for this KV head, loaded with the block
 };
 
 template <int KV>
@@ -102,7 +103,17 @@ __device__ __forceinline__ u32x4 as_bf16x8(const Raw<KV>& r, int s) {
   }
 }
 
-template <int KV, int NG>
+// LDS ordering inside one wave: LDS instructions of a wave execute in issue
+// order, so only the compiler must be kept from moving LDS accesses across
+// this point, and the writes must have completed.  No s_barrier and no wait
+// on outstanding global loads (a workgroup fence would add vmcnt(0) and
+// drain the prefetched blocks).
+__device__ __forceinline__ void lds_wave_sync() {
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0); vmcnt and expcnt untouched
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+template <int KV, int NG, int DEPTH>
 __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
   __shared__ u32x4 lds_k[kBS * 16];  // 16 token rows x 16 chunks of 16 B
   const int lane = threadIdx.x;
@@ -170,27 +181,35 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
 #pragma unroll
   for (int j = 0; j < 4; ++j) rpos[j] = rtok * 16 + ((4 * j + q4) ^ c);
 
-  Raw<KV> kr, vr, kn, vn;
-  {
-    const int p0 = __builtin_amdgcn_readlane(my_blk, 0);
-    load_raw<KV>(kr, kbase + p0 * blk_bytes, lane);
-    load_raw<KV>(vr, vbase + p0 * blk_bytes, lane);
-  }
-
-  for (int i = 0; i < nblk; ++i) {
-    const int p = __builtin_amdgcn_readlane(my_blk, i);
-    if (i + 1 < nblk) {
-      const int pn = __builtin_amdgcn_readlane(my_blk, i + 1);
-      load_raw<KV>(kn, kbase + pn * blk_bytes, lane);
-      load_raw<KV>(vn, vbase + pn * blk_bytes, lane);
+  // Loads run DEPTH blocks ahead of the block being processed.  The step
+  // count is padded to a multiple of DEPTH + 1 so that every unrolled step
+  // issues and processes unconditionally: a load past the partition's last
+  // block re-reads that block (an L2 hit), and a padded step sees no valid
+  // position, which leaves the running max, sum and output unchanged
+  // (alpha = 1, p = 0, V rows zeroed).  The number of loads in flight -- and
+  // every wait count -- is then the same on every path.
+  const int nsteps = (nblk + DEPTH) / (DEPTH + 1) * (DEPTH + 1);
+  Raw<KV> kbuf[DEPTH + 1], vbuf[DEPTH + 1];
+  auto issue = [&](Raw<KV>& kr, Raw<KV>& vr, int i) {
+    const int p = __builtin_amdgcn_readlane(my_blk, min(i, nblk - 1));
+    load_raw<KV>(kr, kbase + p * blk_bytes, lane);
+    load_raw<KV>(vr, vbase + p * blk_bytes, lane);
+    if constexpr (KV == DT_FP8) {
+      kr.scale = a.k_scale[static_cast<size_t>(p) * a.H_KV + h];
+      vr.scale = a.v_scale[static_cast<size_t>(p) * a.H_KV + h];
     }
-    const int valid = t1 - (t0 + i * kBS);  // valid positions in this block (>= 1)
+    // keep the scheduler from sinking these loads below the block being
+    // processed (that would shrink the distance they run ahead)
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  auto process = [&](const Raw<KV>& kr, const Raw<KV>& vr, int i) {
+    const int valid = t1 - (t0 + i * kBS);  // valid positions in this block (<= 0: padding)
 
     // ---- K: widen, transpose through LDS, QK on the matrix cores
-    __syncthreads();  // previous block's LDS reads are done
 #pragma unroll
     for (int s = 0; s < 4; ++s) lds_k[wpos[s]] = as_bf16x8<KV>(kr, s);
-    __syncthreads();
+    lds_wave_sync();
     bf16x8 ka[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) ka[j] = __builtin_bit_cast(bf16x8, lds_k[rpos[j]]);
@@ -198,8 +217,8 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
     float kscale = a.scale_log2;
     float vscale = 1.0f;
     if constexpr (KV == DT_FP8) {
-      kscale *= a.k_scale[static_cast<size_t>(p) * a.H_KV + h];
-      vscale = a.v_scale[static_cast<size_t>(p) * a.H_KV + h];
+      kscale *= kr.scale;
+      vscale = vr.scale;
     }
 
     // ---- V operands: token q + 4i, dim 8c + n  (zero the invalid rows)
@@ -263,10 +282,17 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
         o[G][nn] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pl, o[G][nn], 0, 0, 0);
       }
     }
+    // the K tile in LDS is rewritten by the next block: keep its reads first
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  };
 
-    if (i + 1 < nblk) {
-      kr = kn;
-      vr = vn;
+#pragma unroll
+  for (int d = 0; d < DEPTH; ++d) issue(kbuf[d], vbuf[d], d);
+  for (int i0 = 0; i0 < nsteps; i0 += DEPTH + 1) {
+#pragma unroll
+    for (int u = 0; u <= DEPTH; ++u) {
+      issue(kbuf[(u + DEPTH) % (DEPTH + 1)], vbuf[(u + DEPTH) % (DEPTH + 1)], i0 + u + DEPTH);
+      process(kbuf[u], vbuf[u], i0 + u);
     }
   }
 
@@ -312,17 +338,25 @@ bool mfma_supports(int q_dtype, int kv_dtype, int d_h, int block_size, int g,
          partition_tokens <= 64 * kBS;
 }
 
-hipError_t launch_decode_mfma(int kv_dtype, const DecodeArgs& a, hipStream_t stream) {
+hipError_t launch_decode_mfma(int kv_dtype, int depth, const DecodeArgs& a, hipStream_t stream) {
   const dim3 grid(a.max_parts, a.H_KV, a.B), block(64);
   const bool two = a.g > 16;
-#define PKV_MF(KV, NG) hipLaunchKernelGGL((decode_mfma_kernel<KV, NG>), grid, block, 0, stream, a)
+#define PKV_MF(KV, NG, D) \
+  hipLaunchKernelGGL((decode_mfma_kernel<KV, NG, D>), grid, block, 0, stream, a)
+#define PKV_MF_D(KV, NG)              \
+  switch (depth) {                    \
+    case 1: PKV_MF(KV, NG, 1); break; \
+    case 3: PKV_MF(KV, NG, 3); break; \
+    default: PKV_MF(KV, NG, 2); break; \
+  }
   if (kv_dtype == DT_BF16) {
-    if (two) PKV_MF(DT_BF16, 2); else PKV_MF(DT_BF16, 1);
+    if (two) { PKV_MF_D(DT_BF16, 2) } else { PKV_MF_D(DT_BF16, 1) }
   } else if (kv_dtype == DT_FP8) {
-    if (two) PKV_MF(DT_FP8, 2); else PKV_MF(DT_FP8, 1);
+    if (two) { PKV_MF_D(DT_FP8, 2) } else { PKV_MF_D(DT_FP8, 1) }
   } else {
     return hipErrorInvalidValue;
   }
+#undef PKV_MF_D
 #undef PKV_MF
   return hipGetLastError();
 }

@@ -91,6 +91,7 @@ class Workload:
     context_lens: torch.Tensor         # int32 [B], after the append
     free_order: torch.Tensor           # int32 [num_blocks - used], ids not in any table
     shared_blocks: int                 # leading table entries shared by every request
+    max_context_len: int               # max of context_lens (host value, for grid sizing)
     k_cache: list = field(default_factory=list)   # per layer [num_blocks, H_KV, bs, d_h]
     v_cache: list = field(default_factory=list)
     k_scale: list = field(default_factory=list)   # per layer fp32 [num_blocks, H_KV] (fp8 only)
@@ -102,10 +103,6 @@ class Workload:
     @property
     def softmax_scale(self) -> float:
         return 1.0 / math.sqrt(self.d_h)
-
-    @property
-    def max_context_len(self) -> int:
-        return int(self.context_lens.max().item())
 
 
 def _draw_lens(cfg, B, gen):
@@ -175,7 +172,8 @@ def make_workload(name: str, device="cpu", seed=None, **overrides) -> Workload:
                  kv_dtype=cfg["kv_dtype"], q_dtype=cfg["q_dtype"], layers=layers,
                  num_blocks=num_blocks, max_blocks_per_seq=max_blocks,
                  block_table=table.to(device), context_lens=lens.to(torch.int32).to(device),
-                 free_order=free_order, shared_blocks=shared)
+                 free_order=free_order, shared_blocks=shared,
+                 max_context_len=int(lens.max().item()))
 
     # 3.. values, per layer, on the target device
     dgen = torch.Generator(device=device)
