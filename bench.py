@@ -145,11 +145,12 @@ def main():
     for r in range(R):
         pools.append([(w.k_cache[L] if r == 0 else w.k_cache[L].clone(),
                        w.v_cache[L] if r == 0 else w.v_cache[L].clone()) for L in range(w.layers)])
+    pkv.set_decode_variant(args.variant)  # the plan depends on the variant
     pt, parts, ws_bytes = pkv.decode_plan(w.B, w.H_Q, w.H_KV, w.d_h, w.block_size,
-                                          w.max_context_len, args.partition)
+                                          w.max_context_len, args.partition,
+                                          pkv.dtype_code(w.q[0]), pkv.dtype_code(w.k_cache[0]))
     work = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
     out = torch.empty((w.B, w.H_Q, w.d_h), dtype=torch.float32, device=dev)
-    pkv.set_decode_variant(args.variant)
     stream = torch.cuda.current_stream()
     ks = w.k_scale or [None] * w.layers
     vs = w.v_scale or [None] * w.layers
@@ -276,7 +277,9 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / PEAK_GBS, 4),
                      "traffic": traffic,
-                     "kernel": "decode_mfma_kernel" if args.variant != 1 else "decode_generic_kernel",
+                     "kernel": {0: "decode_mfma_flat_kernel", 1: "decode_generic_kernel",
+                                2: "decode_mfma_flat_kernel",
+                                3: "decode_mfma_kernel"}[args.variant],
                      "algorithmic_bytes_per_launch": att["total"],
                      "avg_launch_us": round(kern_avg_ms * 1e3, 3)},
         "cpu_baseline": cpu,

@@ -156,16 +156,27 @@ int pkv_kv_append(const void* k_new, const void* v_new, int in_dtype, void* k_ca
                   const int32_t* context_lens, int32_t B, int32_t H_KV, int32_t d_h,
                   int32_t block_size, int32_t num_blocks, pkv_stream_t stream);
 
-/* Partition (split-K) planning for paged_decode_attention.  Each request's
- * positions are cut into partitions of `partition_tokens` positions (a
- * multiple of block_size; 0 picks the library default for this shape).
- * *partition_tokens_out receives the value used, *max_partitions_out =
- * ceil(max_context_len / partition_tokens), and *workspace_bytes the
- * device workspace paged_decode_attention needs (0 when every request fits
- * one partition). */
+/* Work split (split-K) planning for paged_decode_attention.  The attention
+ * kernels cut each request's positions into pieces whose partial results a
+ * combine kernel merges:
+ *   - the MFMA kernel (default where it applies: d_h = 128, block_size = 16,
+ *     BF16 query with a BF16 or FP8 cache, H_Q / H_KV <= 32, B <= 8192)
+ *     splits the blocks of all (request, KV head) sequences into one equal
+ *     chunk per wave the device holds at once, so every wave reads the same
+ *     number of blocks whatever the length mix;
+ *   - the generic kernel (and the MFMA kernel when forced with
+ *     PKV_VARIANT_MFMA_PARTITION) cut each request into partitions of
+ *     `partition_tokens` positions (a multiple of block_size; 0 picks the
+ *     library default for this shape).
+ * *partition_tokens_out receives the partition length used by the
+ * partition kernels, *max_partitions_out = ceil(max_context_len /
+ * partition_tokens), and *workspace_bytes the device workspace the
+ * attention call needs for these shapes and dtypes on the current device
+ * (0 when no partial results can arise).  The result depends on the
+ * variant selected by pkv_set_decode_variant at the time of the call. */
 int pkv_decode_plan(int32_t B, int32_t H_Q, int32_t H_KV, int32_t d_h, int32_t block_size,
-                    int32_t max_context_len, int32_t partition_tokens,
-                    int32_t* partition_tokens_out, int32_t* max_partitions_out,
+                    int32_t max_context_len, int32_t partition_tokens, int q_dtype,
+                    int kv_dtype, int32_t* partition_tokens_out, int32_t* max_partitions_out,
                     size_t* workspace_bytes);
 
 /* Paged decode attention (page 1 section 21.1: every query head normalises
@@ -179,10 +190,11 @@ int pkv_decode_plan(int32_t B, int32_t H_Q, int32_t H_KV, int32_t d_h, int32_t b
  * values (they may hold anything, NaN included).  `max_context_len` (a host
  * value) must be >= every context_lens[b]; it sizes the grid.  Supported
  * (q_dtype, kv_dtype): (F32, F32), (BF16, BF16), (BF16, FP8_E4M3).
- * `workspace` holds per-partition partial results when a request spans
- * more than one partition; its size comes from pkv_decode_plan (WORKSPACE
- * if too small).  Launches the partition kernel and, when any request can
- * span more than one partition, the combine kernel. */
+ * `workspace` holds partial results of requests whose positions are split
+ * over several waves; its size comes from pkv_decode_plan with the same
+ * arguments (WORKSPACE if too small; it may be NULL when the plan says 0).
+ * Launches the partition kernel and, when partial results can arise, the
+ * combine kernel.  Calls that share one workspace must not overlap. */
 int pkv_paged_decode_attention(float* out, const void* q, int q_dtype, const void* k_cache,
                                const void* v_cache, int kv_dtype, const float* k_scale,
                                const float* v_scale, const int32_t* block_table,
@@ -193,13 +205,15 @@ int pkv_paged_decode_attention(float* out, const void* q, int q_dtype, const voi
                                size_t workspace_bytes, pkv_stream_t stream);
 
 /* The two launches of pkv_paged_decode_attention, callable separately (for
- * timing each kernel).  decode_partitions runs the per-partition online
- * softmax (same arguments); it writes `out` directly for requests that fit
- * one partition and partial (max, sum, unnormalised output) triples to the
- * workspace otherwise.  combine_partitions merges those partials with the
- * log-sum-exp rule: M = max_p m_p, out = sum_p o_p e^(m_p - M) /
- * sum_p l_p e^(m_p - M).  Call it with the same B, H_Q, d_h, block size,
- * partition and max_context_len as decode_partitions. */
+ * timing each kernel).  decode_partitions runs the online softmax over each
+ * piece (same arguments); it writes `out` directly for requests whose
+ * positions one wave covers and partial (max, sum, unnormalised output)
+ * triples to the workspace otherwise, with a header saying which layout it
+ * used.  combine_partitions merges those partials with the log-sum-exp
+ * rule: M = max_p m_p, out = sum_p o_p e^(m_p - M) / sum_p l_p e^(m_p - M).
+ * Call it right after decode_partitions, on the same stream, with the same
+ * context_lens, max_context_len, B, H_Q, H_KV, d_h, block size, partition
+ * and workspace; with a NULL workspace it does nothing. */
 int pkv_decode_partitions(float* out, const void* q, int q_dtype, const void* k_cache,
                           const void* v_cache, int kv_dtype, const float* k_scale,
                           const float* v_scale, const int32_t* block_table,
@@ -214,11 +228,17 @@ int pkv_combine_partitions(float* out, const int32_t* context_lens, int32_t max_
                            size_t workspace_bytes, pkv_stream_t stream);
 
 /* Kernel selection for the attention calls (process-wide, not
- * thread-safe).  AUTO uses the MFMA kernel where it applies (d_h = 128,
- * block_size = 16, BF16 query with BF16 or FP8 cache, H_Q / H_KV <= 32) and
- * the generic VALU kernel otherwise; GENERIC and MFMA force one (MFMA
- * returns UNSUPPORTED outside its shapes).  Returns the previous value. */
-typedef enum { PKV_VARIANT_AUTO = 0, PKV_VARIANT_GENERIC = 1, PKV_VARIANT_MFMA = 2 } pkv_variant;
+ * thread-safe).  AUTO uses the MFMA kernel with the balanced per-wave split
+ * where it applies and the generic VALU kernel otherwise; GENERIC, MFMA
+ * (balanced split) and MFMA_PARTITION (fixed partitions) force one, and
+ * return UNSUPPORTED from the plan and attention calls outside their
+ * shapes.  Returns the previous value. */
+typedef enum {
+  PKV_VARIANT_AUTO = 0,
+  PKV_VARIANT_GENERIC = 1,
+  PKV_VARIANT_MFMA = 2,
+  PKV_VARIANT_MFMA_PARTITION = 3
+} pkv_variant;
 int pkv_set_decode_variant(int variant);
 
 #ifdef __cplusplus

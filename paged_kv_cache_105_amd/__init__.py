@@ -13,12 +13,17 @@ import ctypes as C
 
 from . import _lib
 from ._lib import (PKV_BF16, PKV_F32, PKV_FP8_E4M3, PKV_VARIANT_AUTO, PKV_VARIANT_GENERIC,
-                   PKV_VARIANT_MFMA, PkvError, check, load)
+                   PKV_VARIANT_MFMA, PKV_VARIANT_MFMA_PARTITION, PkvError, check, load)
 
 __all__ = ["kv_append", "decode_plan", "paged_decode_attention", "decode_partitions",
            "combine_partitions", "set_decode_variant", "BlockPool", "PkvError", "load",
            "PKV_F32", "PKV_BF16", "PKV_FP8_E4M3", "PKV_VARIANT_AUTO", "PKV_VARIANT_GENERIC",
-           "PKV_VARIANT_MFMA"]
+           "PKV_VARIANT_MFMA", "PKV_VARIANT_MFMA_PARTITION", "dtype_code"]
+
+
+def dtype_code(t) -> int:
+    """pkv_dtype of a tensor (float32, bfloat16, float8_e4m3fn / uint8)."""
+    return _dtype_code(t)
 
 
 def _dtype_code(t) -> int:
@@ -60,11 +65,15 @@ def kv_append(k_new, v_new, k_cache, v_cache, block_table, context_lens,
                                _stream(stream)), "pkv_kv_append")
 
 
-def decode_plan(B, H_Q, H_KV, d_h, block_size, max_context_len, partition_tokens=0):
-    """pkv_decode_plan -> (partition_tokens, max_partitions, workspace_bytes)."""
+def decode_plan(B, H_Q, H_KV, d_h, block_size, max_context_len, partition_tokens=0,
+                q_dtype=PKV_BF16, kv_dtype=PKV_BF16):
+    """pkv_decode_plan -> (partition_tokens, max_partitions, workspace_bytes).
+
+    q_dtype / kv_dtype are pkv_dtype codes (see dtype_code)."""
     pt, parts, ws = C.c_int32(), C.c_int32(), C.c_size_t()
     check(load().pkv_decode_plan(B, H_Q, H_KV, d_h, block_size, max_context_len,
-                                 partition_tokens, C.byref(pt), C.byref(parts), C.byref(ws)),
+                                 partition_tokens, int(q_dtype), int(kv_dtype), C.byref(pt),
+                                 C.byref(parts), C.byref(ws)),
           "pkv_decode_plan")
     return pt.value, parts.value, ws.value
 

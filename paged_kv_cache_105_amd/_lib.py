@@ -17,7 +17,7 @@ PKV_OK = 0
 STATUS_NAMES = {0: "ok", -1: "invalid_arg", -2: "out_of_blocks", -3: "bad_block",
                 -4: "shared_block", -5: "hip", -6: "workspace", -7: "unsupported"}
 PKV_F32, PKV_BF16, PKV_FP8_E4M3 = 0, 1, 2
-PKV_VARIANT_AUTO, PKV_VARIANT_GENERIC, PKV_VARIANT_MFMA = 0, 1, 2
+PKV_VARIANT_AUTO, PKV_VARIANT_GENERIC, PKV_VARIANT_MFMA, PKV_VARIANT_MFMA_PARTITION = 0, 1, 2, 3
 
 _i32 = C.c_int32
 _pi32 = C.POINTER(C.c_int32)
@@ -43,8 +43,8 @@ SIGNATURES = {
     "pkv_seq_release": (C.c_int, [_vp, _pi32, _i32]),
     "pkv_kv_append": (C.c_int, [_vp, _vp, C.c_int, _vp, _vp, C.c_int, _vp, _vp, _vp, _i32, _vp,
                                 _i32, _i32, _i32, _i32, _i32, _vp]),
-    "pkv_decode_plan": (C.c_int, [_i32, _i32, _i32, _i32, _i32, _i32, _i32, _pi32, _pi32,
-                                  C.POINTER(_sz)]),
+    "pkv_decode_plan": (C.c_int, [_i32, _i32, _i32, _i32, _i32, _i32, _i32, C.c_int, C.c_int,
+                                  _pi32, _pi32, C.POINTER(_sz)]),
     "pkv_paged_decode_attention": (C.c_int, [_vp, _vp, C.c_int, _vp, _vp, C.c_int, _vp, _vp,
                                              _vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
                                              _i32, _f, _i32, _vp, _sz, _vp]),

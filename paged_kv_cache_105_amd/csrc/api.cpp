@@ -8,6 +8,9 @@
 #include <cmath>
 #include <cstdint>
 #include <cstdlib>
+#include <map>
+#include <mutex>
+#include <tuple>
 
 #include "pkv.h"
 #include "pkv_device.h"
@@ -21,11 +24,13 @@ hipError_t launch_kv_append(int in_dtype, int kv_dtype, const void* k_new, const
 hipError_t launch_decode_generic(int q_dtype, int kv_dtype, const DecodeArgs& a,
                                  hipStream_t stream);
 size_t generic_lds_bytes(int g, int d_h, int partition_tokens);
-bool mfma_supports(int q_dtype, int kv_dtype, int d_h, int block_size, int g,
-                   int partition_tokens);
-hipError_t launch_decode_mfma(int kv_dtype, int depth, const DecodeArgs& a, hipStream_t stream);
-hipError_t launch_combine(float* out, const int32_t* context_lens, Workspace ws, int B, int H_Q,
-                          int d_h, int partition_tokens, int max_parts, hipStream_t stream);
+bool mfma_supports(int q_dtype, int kv_dtype, int d_h, int block_size, int g);
+int mfma_flat_waves(int kv_dtype, int g, int depth, int B);
+hipError_t launch_decode_mfma(int kv_dtype, int depth, bool flat, int waves, const DecodeArgs& a,
+                              hipStream_t stream);
+hipError_t launch_combine(float* out, const int32_t* context_lens, const void* ws, int B, int H_Q,
+                          int H_KV, int d_h, int partition_tokens, int max_parts,
+                          hipStream_t stream);
 }  // namespace pkv
 
 namespace {
@@ -46,11 +51,8 @@ int prefetch_depth() {
 constexpr int kMaxDh = 256;
 constexpr int kMaxGenericPartition = 256;
 constexpr size_t kMaxGenericLds = 64 * 1024;
-constexpr size_t kAlign = 256;
 
 bool valid_dtype(int d) { return d == PKV_F32 || d == PKV_BF16 || d == PKV_FP8_E4M3; }
-
-size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 // Default partition length: enough workgroups to cover the chip several
 // times over, but no shorter than 4 blocks and no longer than 256 positions
@@ -71,29 +73,82 @@ int resolve_partition(int B, int H_KV, int block_size, int max_context_len, int 
   return default_partition(B, H_KV, block_size, max_context_len);
 }
 
+// Largest batch the flat kernel takes: its per-request block prefix lives in
+// LDS (4 bytes per request).
+constexpr int kMaxFlatBatch = 8192;
+constexpr int kMfmaMaxPartition = 64 * 16;
+
+enum Kernel { K_GENERIC = 0, K_MFMA_PARTITION = 1, K_MFMA_FLAT = 2 };
+
 struct Plan {
+  Kernel kernel;
   int partition_tokens;
   int max_parts;
-  size_t o_bytes, ml_bytes, total;
+  int waves;      // flat kernel grid
+  size_t total;   // workspace bytes (0: none needed)
 };
 
+int flat_waves_cached(int kv_dtype, int g, int depth, int B) {
+  // the occupancy query depends on the kernel instance and its LDS size
+  static std::mutex mu;
+  static std::map<std::tuple<int, int, int, int, int>, int> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    (void)hipGetLastError();
+    dev = -1;
+  }
+  const auto key = std::make_tuple(dev, kv_dtype, g > 16 ? 2 : 1, depth, B);
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = cache.find(key);
+  if (it != cache.end()) return it->second;
+  const int w = pkv::mfma_flat_waves(kv_dtype, g, depth, B);
+  cache[key] = w;
+  return w;
+}
+
 int make_plan(int B, int H_Q, int H_KV, int d_h, int block_size, int max_context_len,
-              int partition_tokens, Plan* plan) {
+              int partition_tokens, int q_dtype, int kv_dtype, Plan* plan) {
   if (B < 1 || H_Q < 1 || H_KV < 1 || H_Q % H_KV || d_h < 1 || d_h > kMaxDh || block_size < 1 ||
-      max_context_len < 1 || partition_tokens < 0)
+      max_context_len < 1 || partition_tokens < 0 || !valid_dtype(q_dtype) ||
+      !valid_dtype(kv_dtype))
     return PKV_ERR_INVALID_ARG;
+  if (B > 65535 || H_KV > 65535 || H_Q > 65535) return PKV_ERR_INVALID_ARG;
+  const int g = H_Q / H_KV;
   const int pt = resolve_partition(B, H_KV, block_size, max_context_len, partition_tokens);
   if (pt % block_size) return PKV_ERR_INVALID_ARG;
   plan->partition_tokens = pt;
   plan->max_parts = (max_context_len + pt - 1) / pt;
-  // grid.x limit of the launch and the combine kernel's LDS weight array (64 KiB)
-  if (plan->max_parts > 16384) return PKV_ERR_INVALID_ARG;
-  if (plan->max_parts == 1) {
-    plan->o_bytes = plan->ml_bytes = plan->total = 0;
+  if (plan->max_parts > 65535) return PKV_ERR_INVALID_ARG;  // grid.x of the launch
+  plan->waves = 0;
+
+  const bool mfma_ok = pkv::mfma_supports(q_dtype, kv_dtype, d_h, block_size, g);
+  switch (g_variant) {
+    case PKV_VARIANT_GENERIC:
+      plan->kernel = K_GENERIC;
+      break;
+    case PKV_VARIANT_MFMA:
+      if (!mfma_ok || B > kMaxFlatBatch) return PKV_ERR_UNSUPPORTED;
+      plan->kernel = K_MFMA_FLAT;
+      break;
+    case PKV_VARIANT_MFMA_PARTITION:
+      if (!mfma_ok) return PKV_ERR_UNSUPPORTED;
+      plan->kernel = K_MFMA_PARTITION;
+      break;
+    default:
+      plan->kernel = !mfma_ok ? K_GENERIC : (B <= kMaxFlatBatch ? K_MFMA_FLAT : K_MFMA_PARTITION);
+  }
+  if (plan->kernel == K_GENERIC &&
+      (pt > kMaxGenericPartition || pkv::generic_lds_bytes(g, d_h, pt) > kMaxGenericLds))
+    return PKV_ERR_UNSUPPORTED;
+  if (plan->kernel == K_MFMA_PARTITION && pt > kMfmaMaxPartition) return PKV_ERR_UNSUPPORTED;
+
+  if (plan->kernel == K_MFMA_FLAT) {
+    plan->waves = flat_waves_cached(kv_dtype, g, prefetch_depth(), B);
+    plan->total = pkv::flat_layout(B, plan->waves, g, d_h).total;
+  } else if (plan->max_parts == 1) {
+    plan->total = 0;
   } else {
-    plan->o_bytes = align_up(sizeof(float) * pkv::ws_o_floats(B, H_Q, plan->max_parts, d_h));
-    plan->ml_bytes = align_up(sizeof(float) * pkv::ws_ml_floats(B, H_Q, plan->max_parts));
-    plan->total = plan->o_bytes + plan->ml_bytes;
+    plan->total = pkv::partition_layout(B, H_Q, plan->max_parts, d_h).total;
   }
   return PKV_OK;
 }
@@ -149,12 +204,12 @@ const char* pkv_status_string(int status) {
   }
 }
 
-int pkv_abi_version(void) { return 1; }
+int pkv_abi_version(void) { return 2; }
 
 int pkv_set_decode_variant(int variant) {
   const int prev = g_variant;
   if (variant == PKV_VARIANT_AUTO || variant == PKV_VARIANT_GENERIC ||
-      variant == PKV_VARIANT_MFMA)
+      variant == PKV_VARIANT_MFMA || variant == PKV_VARIANT_MFMA_PARTITION)
     g_variant = variant;
   return prev;
 }
@@ -181,12 +236,12 @@ int pkv_kv_append(const void* k_new, const void* v_new, int in_dtype, void* k_ca
 }
 
 int pkv_decode_plan(int32_t B, int32_t H_Q, int32_t H_KV, int32_t d_h, int32_t block_size,
-                    int32_t max_context_len, int32_t partition_tokens,
+                    int32_t max_context_len, int32_t partition_tokens, int q_dtype, int kv_dtype,
                     int32_t* partition_tokens_out, int32_t* max_partitions_out,
                     size_t* workspace_bytes) {
   Plan plan;
-  const int st =
-      make_plan(B, H_Q, H_KV, d_h, block_size, max_context_len, partition_tokens, &plan);
+  const int st = make_plan(B, H_Q, H_KV, d_h, block_size, max_context_len, partition_tokens,
+                           q_dtype, kv_dtype, &plan);
   if (st != PKV_OK) return st;
   if (partition_tokens_out) *partition_tokens_out = plan.partition_tokens;
   if (max_partitions_out) *max_partitions_out = plan.max_parts;
@@ -207,10 +262,13 @@ int pkv_decode_partitions(float* out, const void* q, int q_dtype, const void* k_
                                 B, H_Q, H_KV, d_h, block_size, num_blocks, softmax_scale);
   if (st != PKV_OK) return st;
   Plan plan;
-  st = make_plan(B, H_Q, H_KV, d_h, block_size, max_context_len, partition_tokens, &plan);
+  st = make_plan(B, H_Q, H_KV, d_h, block_size, max_context_len, partition_tokens, q_dtype,
+                 kv_dtype, &plan);
   if (st != PKV_OK) return st;
   if (plan.total > 0 && (!workspace || workspace_bytes < plan.total)) return PKV_ERR_WORKSPACE;
   if (reinterpret_cast<uintptr_t>(workspace) & 15) return PKV_ERR_INVALID_ARG;
+  // a workspace too small to hold the header is not used at all
+  if (workspace_bytes < pkv::kWsHeader) workspace = nullptr;
 
   pkv::DecodeArgs a{};
   a.out = out;
@@ -221,9 +279,7 @@ int pkv_decode_partitions(float* out, const void* q, int q_dtype, const void* k_
   a.v_scale = v_scale;
   a.block_table = block_table;
   a.context_lens = context_lens;
-  a.ws.o = plan.total ? static_cast<float*>(workspace) : nullptr;
-  a.ws.ml = plan.total ? reinterpret_cast<float*>(static_cast<char*>(workspace) + plan.o_bytes)
-                       : nullptr;
+  a.ws = static_cast<char*>(workspace);
   a.max_blocks_per_seq = max_blocks_per_seq;
   a.B = B;
   a.H_Q = H_Q;
@@ -235,25 +291,18 @@ int pkv_decode_partitions(float* out, const void* q, int q_dtype, const void* k_
   a.partition_tokens = plan.partition_tokens;
   a.max_parts = plan.max_parts;
   a.scale_log2 = softmax_scale * pkv::kLog2e;
-  if (B > 65535 || H_KV > 65535) return PKV_ERR_INVALID_ARG;
 
-  const bool mfma_ok = pkv::mfma_supports(q_dtype, kv_dtype, d_h, block_size, a.g,
-                                          plan.partition_tokens);
-  bool use_mfma = false;
-  if (g_variant == PKV_VARIANT_MFMA) {
-    if (!mfma_ok) return PKV_ERR_UNSUPPORTED;
-    use_mfma = true;
-  } else if (g_variant == PKV_VARIANT_AUTO) {
-    use_mfma = mfma_ok;
-  }
   hipError_t e;
-  if (use_mfma) {
-    e = pkv::launch_decode_mfma(kv_dtype, prefetch_depth(), a, static_cast<hipStream_t>(stream));
-  } else {
-    if (plan.partition_tokens > kMaxGenericPartition ||
-        pkv::generic_lds_bytes(a.g, d_h, plan.partition_tokens) > kMaxGenericLds)
-      return PKV_ERR_UNSUPPORTED;
-    e = pkv::launch_decode_generic(q_dtype, kv_dtype, a, static_cast<hipStream_t>(stream));
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  switch (plan.kernel) {
+    case K_MFMA_FLAT:
+      e = pkv::launch_decode_mfma(kv_dtype, prefetch_depth(), true, plan.waves, a, s);
+      break;
+    case K_MFMA_PARTITION:
+      e = pkv::launch_decode_mfma(kv_dtype, prefetch_depth(), false, 0, a, s);
+      break;
+    default:
+      e = pkv::launch_decode_generic(q_dtype, kv_dtype, a, s);
   }
   return hip_status(e);
 }
@@ -263,19 +312,17 @@ int pkv_combine_partitions(float* out, const int32_t* context_lens, int32_t max_
                            int32_t block_size, int32_t partition_tokens, const void* workspace,
                            size_t workspace_bytes, pkv_stream_t stream) {
   if (!out || !context_lens) return PKV_ERR_INVALID_ARG;
-  Plan plan;
-  const int st =
-      make_plan(B, H_Q, H_KV, d_h, block_size, max_context_len, partition_tokens, &plan);
-  if (st != PKV_OK) return st;
-  if (plan.max_parts == 1) return PKV_OK;  // nothing to merge
-  if (!workspace || workspace_bytes < plan.total) return PKV_ERR_WORKSPACE;
-  if (B > 65535 || H_Q > 65535) return PKV_ERR_INVALID_ARG;
-  pkv::Workspace ws;
-  ws.o = static_cast<float*>(const_cast<void*>(workspace));
-  ws.ml = reinterpret_cast<float*>(static_cast<char*>(const_cast<void*>(workspace)) + plan.o_bytes);
-  return hip_status(pkv::launch_combine(out, context_lens, ws, B, H_Q, d_h,
-                                        plan.partition_tokens, plan.max_parts,
-                                        static_cast<hipStream_t>(stream)));
+  if (B < 1 || H_Q < 1 || H_KV < 1 || H_Q % H_KV || d_h < 1 || d_h > kMaxDh || block_size < 1 ||
+      max_context_len < 1 || partition_tokens < 0 || B > 65535 || H_Q > 65535)
+    return PKV_ERR_INVALID_ARG;
+  // without a workspace no partial can exist: the partition call wrote out
+  if (!workspace || workspace_bytes < pkv::kWsHeader) return PKV_OK;
+  const int pt = resolve_partition(B, H_KV, block_size, max_context_len, partition_tokens);
+  if (pt % block_size) return PKV_ERR_INVALID_ARG;
+  const int max_parts = (max_context_len + pt - 1) / pt;
+  // the workspace header written by the partition call selects the layout
+  return hip_status(pkv::launch_combine(out, context_lens, workspace, B, H_Q, H_KV, d_h, pt,
+                                        max_parts, static_cast<hipStream_t>(stream)));
 }
 
 int pkv_paged_decode_attention(float* out, const void* q, int q_dtype, const void* k_cache,
@@ -291,6 +338,11 @@ int pkv_paged_decode_attention(float* out, const void* q, int q_dtype, const voi
                                  B, H_Q, H_KV, d_h, block_size, num_blocks, softmax_scale,
                                  partition_tokens, workspace, workspace_bytes, stream);
   if (st != PKV_OK) return st;
+  Plan plan;
+  st = make_plan(B, H_Q, H_KV, d_h, block_size, max_context_len, partition_tokens, q_dtype,
+                 kv_dtype, &plan);
+  if (st != PKV_OK) return st;
+  if (plan.total == 0) return PKV_OK;  // one partition per request: out is final
   return pkv_combine_partitions(out, context_lens, max_context_len, B, H_Q, H_KV, d_h,
                                 block_size, partition_tokens, workspace, workspace_bytes,
                                 stream);

@@ -33,6 +33,13 @@ __global__ __launch_bounds__(256) void decode_generic_kernel(DecodeArgs a) {
   extern __shared__ float smem[];
   const int part = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int g = a.g, d_h = a.d_h, bs = a.block_size, PT = a.partition_tokens;
+  if (part == 0 && h == 0 && b == 0 && threadIdx.x == 0 && a.ws) {
+    WsHeader* hd = reinterpret_cast<WsHeader*>(a.ws);
+    hd->mode = kWsPartition;
+    hd->waves = 0;
+    hd->B = a.B;
+    hd->g = g;
+  }
   const int n_raw = a.context_lens[b];
   const int n = min(n_raw, a.max_blocks_per_seq * bs);   // never read past the table row
   const int t0 = part * PT;
@@ -101,11 +108,14 @@ __global__ __launch_bounds__(256) void decode_generic_kernel(DecodeArgs a) {
     if (nparts == 1) {
       a.out[hq * d_h + d] = acc / ml_s[2 * j + 1];
     } else {
+      const PartitionLayout PL = partition_layout(a.B, a.H_Q, a.max_parts, d_h);
+      float* wo = reinterpret_cast<float*>(a.ws + PL.o);
+      float* wml = reinterpret_cast<float*>(a.ws + PL.ml);
       const size_t slot = hq * a.max_parts + part;
-      a.ws.o[slot * d_h + d] = acc;
+      wo[slot * d_h + d] = acc;
       if (d == 0) {
-        a.ws.ml[2 * slot] = ml_s[2 * j];
-        a.ws.ml[2 * slot + 1] = ml_s[2 * j + 1];
+        wml[2 * slot] = ml_s[2 * j];
+        wml[2 * slot + 1] = ml_s[2 * j + 1];
       }
     }
   }

@@ -74,22 +74,67 @@ __device__ __forceinline__ float load_elem(const void* base, size_t idx) {
   }
 }
 
-// Partial results of one (request, query head, partition), shared by the
-// partition kernels and the combine kernel:
-//   ws_o [B][H_Q][max_parts][d_h]  unnormalised sum_t 2^(s2_t - m) V_t
-//   ws_ml[B][H_Q][max_parts][2]    (m, l) with m = max_t s2_t and
-//                                  l = sum_t 2^(s2_t - m),
+// Workspace of the attention call.  It starts with a 256-byte header the
+// partition kernels write and the combine kernel reads, so the combine knows
+// which of the two partial layouts it has to merge:
+//
+//   partition layout (kWsPartition): one partial per (request, query head,
+//     partition of partition_tokens positions):
+//       o [B][H_Q][max_parts][d_h]   unnormalised sum_t 2^(s2_t - m) V_t
+//       ml[B][H_Q][max_parts][2]     (m, l): m = max_t s2_t, l = sum_t 2^(s2_t - m)
+//   flat layout (kWsFlat): the blocks of all (request, KV head) sequences,
+//     concatenated request-major, are cut into C = min(W, T) equal chunks of
+//     at least one block, one per wave (waves w >= C idle);
+//     a wave writes at most two partials (slot 0: its first sequence, slot 1:
+//     its last one) for the sequences its chunk cuts, each for all g heads:
+//       prefix[B + 1]                blocks of requests 0..b-1 (int32)
+//       ml[W][2][g][2], o[W][2][g][d_h]
 // where s2_t = softmax_scale * log2(e) * q . k_t (log2 units).
-struct Workspace {
-  float* o;
-  float* ml;
+constexpr int kWsPartition = 1;
+constexpr int kWsFlat = 2;
+constexpr size_t kWsHeader = 256;
+constexpr size_t kWsAlign = 256;
+
+struct WsHeader {
+  int32_t mode;
+  int32_t waves;   // flat layout: grid size W (sizes the partial arrays)
+  int32_t B;
+  int32_t g;
+  int32_t chunks;  // flat layout: chunks actually used, min(W, T) (T = total blocks)
 };
 
-__host__ __device__ inline size_t ws_o_floats(int B, int H_Q, int parts, int d_h) {
-  return static_cast<size_t>(B) * H_Q * parts * d_h;
+__host__ __device__ inline size_t ws_align(size_t x) { return (x + kWsAlign - 1) / kWsAlign * kWsAlign; }
+
+struct PartitionLayout {
+  size_t o, ml, total;  // byte offsets from the workspace start, total size
+};
+__host__ __device__ inline PartitionLayout partition_layout(int B, int H_Q, int parts, int d_h) {
+  PartitionLayout L;
+  L.o = kWsHeader;
+  L.ml = L.o + ws_align(sizeof(float) * static_cast<size_t>(B) * H_Q * parts * d_h);
+  L.total = L.ml + ws_align(sizeof(float) * static_cast<size_t>(B) * H_Q * parts * 2);
+  return L;
 }
-__host__ __device__ inline size_t ws_ml_floats(int B, int H_Q, int parts) {
-  return static_cast<size_t>(B) * H_Q * parts * 2;
+
+struct FlatLayout {
+  size_t prefix, ml, o, total;
+};
+__host__ __device__ inline FlatLayout flat_layout(int B, int W, int g, int d_h) {
+  FlatLayout L;
+  L.prefix = kWsHeader;
+  L.ml = L.prefix + ws_align(sizeof(int32_t) * (static_cast<size_t>(B) + 1));
+  L.o = L.ml + ws_align(sizeof(float) * static_cast<size_t>(W) * 2 * g * 2);
+  L.total = L.o + ws_align(sizeof(float) * static_cast<size_t>(W) * 2 * g * d_h);
+  return L;
+}
+
+// The chunk [floor(w T / C), floor((w + 1) T / C)) holding block x (C <= T,
+// so no chunk is empty).
+__host__ __device__ inline int flat_wave_of(long long x, long long T, int W) {
+  return static_cast<int>(((x + 1) * W - 1) / T);
+}
+__host__ __device__ inline long long flat_chunk_lo(int w, long long T, int W) {
+  return static_cast<long long>(w) * T / W;
 }
 
 struct DecodeArgs {
@@ -101,7 +146,7 @@ struct DecodeArgs {
   const float* v_scale;
   const int32_t* block_table;
   const int32_t* context_lens;
-  Workspace ws;
+  char* ws;  // workspace base (header first)
   int32_t max_blocks_per_seq;
   int32_t B, H_Q, H_KV, g, d_h, block_size, num_blocks;
   int32_t partition_tokens, max_parts;

@@ -39,7 +39,7 @@ def test_status_strings():
     lib = pkv.load()
     assert lib.pkv_status_string(0) == b"ok"
     assert lib.pkv_status_string(-2) == b"out of blocks"
-    assert lib.pkv_abi_version() == 1
+    assert lib.pkv_abi_version() == 2
 
 
 def _row(n):

@@ -23,6 +23,8 @@ from paged_kv_cache_105_amd.workloads import as_numpy, make_workload
 pytestmark = pytest.mark.gpu
 TOL = 2e-3
 DEV = torch.device("cuda:0")
+VARIANTS = [pkv.PKV_VARIANT_GENERIC, pkv.PKV_VARIANT_MFMA, pkv.PKV_VARIANT_MFMA_PARTITION]
+VIDS = ["generic", "mfma_flat", "mfma_part"]
 
 
 def _np(w, layer=0):
@@ -48,12 +50,13 @@ def gpu_step(w, layer=0, partition_tokens=0, variant=pkv.PKV_VARIANT_AUTO, kc=No
     vs = g(w.v_scale[layer]) if w.v_scale else None
     if append:
         pkv.kv_append(g(w.k_new[layer]), g(w.v_new[layer]), k_cache, v_cache, bt, cl, ks, vs)
-    _, _, ws = pkv.decode_plan(w.B, w.H_Q, w.H_KV, w.d_h, w.block_size, w.max_context_len,
-                               partition_tokens)
-    work = torch.empty(max(ws, 256), dtype=torch.uint8, device=DEV)
     out = torch.full((w.B, w.H_Q, w.d_h), float("nan"), dtype=torch.float32, device=DEV)
-    prev = pkv.set_decode_variant(variant)
+    prev = pkv.set_decode_variant(variant)  # the plan depends on the variant
     try:
+        _, _, ws = pkv.decode_plan(w.B, w.H_Q, w.H_KV, w.d_h, w.block_size, w.max_context_len,
+                                   partition_tokens, pkv.dtype_code(w.q[layer]),
+                                   pkv.dtype_code(w.k_cache[layer]))
+        work = torch.empty(max(ws, 256), dtype=torch.uint8, device=DEV)
         pkv.paged_decode_attention(out, g(w.q[layer]), k_cache, v_cache, bt, cl,
                                    w.max_context_len, w.softmax_scale, ks, vs,
                                    partition_tokens=partition_tokens, workspace=work)
@@ -127,7 +130,7 @@ def test_fp8_append_exhaustive_bf16_inputs():
     assert np.array_equal(as_numpy(vc), rv)
 
 
-@pytest.mark.parametrize("variant", [pkv.PKV_VARIANT_GENERIC, pkv.PKV_VARIANT_MFMA])
+@pytest.mark.parametrize("variant", VARIANTS, ids=VIDS)
 def test_fp8_every_finite_code_decodes_exactly(variant):
     # n = 1: the output is the appended value itself; with scale 1 the
     # appended bf16 inputs are the exact E4M3 values, so out == code value
@@ -148,7 +151,6 @@ def test_fp8_every_finite_code_decodes_exactly(variant):
 # ---------------------------------------------------------------------------
 
 LENS = [1, 2, 15, 16, 17, 31, 33, 64, 250, 257, 511, 600, 1000, 1025]
-VARIANTS = [pkv.PKV_VARIANT_GENERIC, pkv.PKV_VARIANT_MFMA]
 
 
 @pytest.mark.parametrize("partition", [0, 16, 64, 256])
@@ -163,11 +165,13 @@ def test_tiny_fp32_generic(partition):
         assert e <= TOL
 
 
-@pytest.mark.parametrize("variant", VARIANTS, ids=["generic", "mfma"])
+@pytest.mark.parametrize("variant", VARIANTS, ids=VIDS)
 @pytest.mark.parametrize("partition", [0, 16, 64, 256, 1024])
 def test_llama8b_shapes(variant, partition):
     if variant == pkv.PKV_VARIANT_GENERIC and partition > 256:
         pytest.skip("the generic kernel takes partitions up to 256 positions")
+    if variant == pkv.PKV_VARIANT_MFMA and partition not in (0, 64):
+        pytest.skip("the balanced split does not use the partition length")
     w = make_workload("llama8b", lens_after=LENS)
     _, _, out = gpu_step(w, partition_tokens=partition, variant=variant)
     _, _, ref = oracle_step(w, _np(w))
@@ -176,7 +180,7 @@ def test_llama8b_shapes(variant, partition):
     assert e <= TOL
 
 
-@pytest.mark.parametrize("variant", VARIANTS, ids=["generic", "mfma"])
+@pytest.mark.parametrize("variant", VARIANTS, ids=VIDS)
 @pytest.mark.parametrize("hq_hkv", [(8, 8), (8, 4), (16, 4), (32, 4), (32, 2), (32, 1), (24, 2)])
 def test_group_sizes_bf16(variant, hq_hkv):
     H_Q, H_KV = hq_hkv
@@ -188,7 +192,7 @@ def test_group_sizes_bf16(variant, hq_hkv):
     assert e <= TOL
 
 
-@pytest.mark.parametrize("variant", VARIANTS, ids=["generic", "mfma"])
+@pytest.mark.parametrize("variant", VARIANTS, ids=VIDS)
 @pytest.mark.parametrize("name", ["fp8_mqa", "fp8_gqa", "fp8_mha"])
 def test_fp8_shapes(variant, name):
     w = make_workload(name, lens_after=[1, 16, 17, 129, 700, 2049])
@@ -212,10 +216,28 @@ def test_generic_other_head_dims():
 
 def test_split_partitions_agree_with_one_partition():
     w = make_workload("llama8b", lens_after=[1, 300, 1000, 1024])
-    _, _, one = gpu_step(w, partition_tokens=1024, variant=pkv.PKV_VARIANT_MFMA)
+    _, _, one = gpu_step(w, partition_tokens=1024, variant=pkv.PKV_VARIANT_MFMA_PARTITION)
     for pt in (16, 48, 256):
-        _, _, many = gpu_step(w, partition_tokens=pt)
+        _, _, many = gpu_step(w, partition_tokens=pt, variant=pkv.PKV_VARIANT_MFMA_PARTITION)
         assert np.max(np.abs(one - many)) <= 1e-4
+    _, _, flat = gpu_step(w, variant=pkv.PKV_VARIANT_MFMA)
+    assert np.max(np.abs(one - flat)) <= 1e-4
+
+
+@pytest.mark.parametrize("lens", [[1] * 300 + [5000], [16] * 64 + [1, 2, 3], [40000],
+                                  [1, 1, 1], list(range(1, 129))])
+def test_balanced_split_edge_cases(lens):
+    # the balanced split cuts the concatenated block sequences into one chunk
+    # per resident wave: many 1-block sequences inside one chunk, one long
+    # sequence over hundreds of chunks, more waves than blocks
+    w = make_workload("llama8b", lens_after=lens, H_Q=8, H_KV=2)
+    _, _, out = gpu_step(w, variant=pkv.PKV_VARIANT_MFMA)
+    req = sorted(set([0, len(lens) // 2, len(lens) - 1]))
+    _, _, ref = oracle_step(w, _np(w), requests=req)
+    e = _err(out, ref, req)
+    _log(f"flat edge {len(lens)} reqs err={e:.2e}")
+    assert e <= TOL
+    assert np.all(np.isfinite(out))
 
 
 def test_run_to_run_bitwise_deterministic():
@@ -286,7 +308,7 @@ def test_shared_versus_private_prefix_bitwise():
     assert _err(shared, ref) <= TOL
 
 
-@pytest.mark.parametrize("variant", VARIANTS, ids=["generic", "mfma"])
+@pytest.mark.parametrize("variant", VARIANTS, ids=VIDS)
 @pytest.mark.parametrize("name", ["llama8b", "fp8_gqa"])
 def test_unused_slots_never_read(variant, name):
     w = make_workload(name, lens_after=[1, 14, 16, 17, 250, 700])
