@@ -101,7 +101,13 @@ int flat_waves_cached(int kv_dtype, int g, int depth, int B) {
   std::lock_guard<std::mutex> lock(mu);
   auto it = cache.find(key);
   if (it != cache.end()) return it->second;
-  const int w = pkv::mfma_flat_waves(kv_dtype, g, depth, B);
+  int w = pkv::mfma_flat_waves(kv_dtype, g, depth, B);
+  // PKV_FLAT_WAVES overrides the grid size of the balanced split, for tuning
+  // measurements (more waves than fit at once only adds a second round)
+  if (const char* e = std::getenv("PKV_FLAT_WAVES")) {
+    const int v = std::atoi(e);
+    if (v >= 1 && v <= (1 << 20)) w = v;
+  }
   cache[key] = w;
   return w;
 }
