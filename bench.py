@@ -155,18 +155,14 @@ def main():
     ks = w.k_scale or [None] * w.layers
     vs = w.v_scale or [None] * w.layers
 
-    def step(r, events=None):
+    def step(r):
         for L in range(w.layers):
             kc, vc = pools[r][L]
             pkv.kv_append(w.k_new[L], w.v_new[L], kc, vc, w.block_table, w.context_lens,
                           ks[L], vs[L], stream=stream)
-            if events is not None:
-                events[0].record(stream)
             pkv.decode_partitions(out, w.q[L], kc, vc, w.block_table, w.context_lens,
                                   w.max_context_len, w.softmax_scale, ks[L], vs[L],
                                   partition_tokens=pt, workspace=work, stream=stream)
-            if events is not None:
-                events[1].record(stream)
             pkv.combine_partitions(out, w.context_lens, w.max_context_len, w.H_KV,
                                    w.block_size, partition_tokens=pt, workspace=work,
                                    stream=stream)
@@ -182,28 +178,26 @@ def main():
     torch.cuda.synchronize()
     ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
 
-    # timed region 2: same steps with HIP events around every partition launch
-    evs = [[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
-           for _ in range(args.steps * w.layers)]
-    torch.cuda.synchronize()
-    k = 0
-    for i in range(args.steps):
-        for L in range(w.layers):
-            kc, vc = pools[i % R][L]
-            pkv.kv_append(w.k_new[L], w.v_new[L], kc, vc, w.block_table, w.context_lens,
-                          ks[L], vs[L], stream=stream)
-            evs[k][0].record(stream)
-            pkv.decode_partitions(out, w.q[L], kc, vc, w.block_table, w.context_lens,
-                                  w.max_context_len, w.softmax_scale, ks[L], vs[L],
-                                  partition_tokens=pt, workspace=work, stream=stream)
-            evs[k][1].record(stream)
-            pkv.combine_partitions(out, w.context_lens, w.max_context_len, w.H_KV,
-                                   w.block_size, partition_tokens=pt, workspace=work,
-                                   stream=stream)
-            k += 1
-    torch.cuda.synchronize()
-    kern_ms = sorted(a.elapsed_time(b) for a, b in evs)
-    kern_avg_ms = sum(kern_ms) / len(kern_ms)
+    # timed region 2: the partition kernel alone, launched back to back over
+    # the rotating pool copies, one HIP event pair on its stream around the
+    # whole batch (per-launch event pairs would add the dispatch latency of
+    # each launch to its time)
+    kern_ms = []
+    for rep in range(3):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for i in range(args.steps):
+            for L in range(w.layers):
+                kc, vc = pools[i % R][L]
+                pkv.decode_partitions(out, w.q[L], kc, vc, w.block_table, w.context_lens,
+                                      w.max_context_len, w.softmax_scale, ks[L], vs[L],
+                                      partition_tokens=pt, workspace=work, stream=stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        kern_ms.append(e0.elapsed_time(e1) / (args.steps * w.layers))
+    kern_ms.sort()
+    kern_avg_ms = kern_ms[len(kern_ms) // 2]
 
     att = metrics.attention_bytes(lens, w.H_Q, w.H_KV, w.d_h, w.block_size, w.kv_dtype,
                                   w.q_dtype)
@@ -214,9 +208,9 @@ def main():
     traffic = measured_traffic(args.workload, pt)
     log(f"partition={pt} parts={parts} workspace={ws_bytes} B; step {ms_per_step * 1e3:.1f} us "
         f"({ms_per_step * 1e3 / w.layers:.1f} us/layer); partition kernel avg "
-        f"{kern_avg_ms * 1e3:.1f} us (p10 {kern_ms[len(kern_ms) // 10] * 1e3:.1f}, p90 "
-        f"{kern_ms[9 * len(kern_ms) // 10] * 1e3:.1f}); KV bytes/layer {att['kv']}; "
-        f"kernel {achieved:.0f} GB/s = {100 * achieved / PEAK_GBS:.1f}% of peak")
+        f"{kern_avg_ms * 1e3:.1f} us (batches: {', '.join(f'{x * 1e3:.1f}' for x in kern_ms)}); "
+        f"KV bytes/layer {att['kv']}; kernel {achieved:.0f} GB/s = "
+        f"{100 * achieved / PEAK_GBS:.1f}% of peak")
 
     # reference bandwidths of plain torch kernels on this machine (context for the
     # % of peak): a 1 GiB device-to-device copy and a 2 GiB read-only sum
