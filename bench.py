@@ -62,6 +62,52 @@ def measured_traffic(workload: str, partition: int):
     return rec.get("hbm_bytes_per_launch")
 
 
+def gather_reference(w, pools, stream, steps, waves=2048):
+    """Achieved bandwidth of a compute-free read of exactly the K/V tiles one
+    attention step reads (libpkv_bench.so), timed like the partition kernel."""
+    import ctypes as C
+
+    import numpy as np
+    import torch
+
+    lib = C.CDLL(os.path.join(ROOT, "paged_kv_cache_105_amd", "libpkv_bench.so"))
+    lib.pkvb_gather_read.restype = C.c_int
+    lib.pkvb_gather_read.argtypes = [C.c_void_p, C.c_void_p, C.c_void_p, C.c_int64, C.c_int32,
+                                     C.c_int32, C.c_void_p, C.c_void_p]
+    tile = w.block_size * w.d_h * (2 if w.kv_dtype == "bf16" else 1)
+    table = w.block_table.cpu().numpy().astype(np.int64)
+    lens = w.context_lens.cpu().numpy()
+    offs = []
+    for b in range(w.B):
+        nb = -(-int(lens[b]) // w.block_size)
+        blk = table[b, :nb]
+        for h in range(w.H_KV):
+            offs.append((blk * w.H_KV + h) * tile)
+    offs = torch.from_numpy(np.concatenate(offs)).to(pools[0][0][0].device)
+    sink = torch.empty(waves * 64 * 4, dtype=torch.int32, device=offs.device)
+    R = len(pools)
+    def run(i):
+        kc, vc = pools[i % R][0]
+        rc = lib.pkvb_gather_read(kc.data_ptr(), vc.data_ptr(), offs.data_ptr(), offs.numel(),
+                                  tile, waves, sink.data_ptr(), stream.cuda_stream)
+        assert rc == 0, rc
+    for i in range(3):
+        run(i)
+    ms = []
+    for rep in range(3):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for i in range(steps):
+            run(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms.append(e0.elapsed_time(e1) / steps)
+    ms.sort()
+    nbytes = 2 * offs.numel() * tile
+    return round(nbytes / (ms[1] * 1e-3) / 1e9, 1)
+
+
 def cpu_baseline(w, layer_tensors, budget_s: float):
     """Time the oracle (as it stands) on a bounded sample: the append of the
     whole batch, then attention request by request until ~budget_s."""
@@ -233,6 +279,10 @@ def main():
     del x, y
     log(f"reference torch kernels: {ref}")
 
+    ref["gather_gbs"] = gather_reference(w, pools, stream, args.steps)
+    log(f"compute-free gather of the same tiles: {ref['gather_gbs']} GB/s "
+        f"(partition kernel at {100 * achieved / ref['gather_gbs']:.1f}% of it)")
+
     if args.calibrate_copy > 0:
         src = torch.ones(args.calibrate_copy * 2 ** 20 // 4, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
@@ -267,7 +317,8 @@ def main():
                    "mean_context": round(sum(lens) / len(lens), 1),
                    "us_per_step_per_layer": round(ms_per_step * 1e3 / w.layers, 2),
                    "pct_of_peak_step": round(100 * value / PEAK_GBS, 2),
-                   "reference_torch_gbs": ref},
+                   "reference_gbs": ref,
+                   "pct_of_gather_reference": round(100 * achieved / ref["gather_gbs"], 1)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / PEAK_GBS, 4),
                      "traffic": traffic,

@@ -15,6 +15,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libpkv.so")
+BENCH_LIB = os.path.join(PKG, "libpkv_bench.so")   # measurement helper of bench.py
 
 HIP_SOURCES = ["kv_append.hip", "decode_generic.hip", "decode_mfma.hip", "combine.hip"]
 CXX_SOURCES = ["api.cpp", "pool.cpp"]
@@ -34,10 +35,8 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source into libpkv.so (always recompiles)."""
-    srcs = [os.path.join(CSRC, s) for s in HIP_SOURCES + CXX_SOURCES]
-    tmp = LIB + ".tmp"
+def _compile(srcs, out, verbose):
+    tmp = out + ".tmp"
     cmd = [hipcc(), *FLAGS, "-I", os.path.join(ROOT, "include"), "-I", CSRC, *srcs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
@@ -48,7 +47,13 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{err}")
     if err.strip() and verbose:
         print(err, file=sys.stderr)
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile libpkv.so and the bench helper libpkv_bench.so (always recompiles)."""
+    _compile([os.path.join(CSRC, s) for s in HIP_SOURCES + CXX_SOURCES], LIB, verbose)
+    _compile([os.path.join(CSRC, "bench_gather.hip")], BENCH_LIB, verbose)
     return LIB
 
 

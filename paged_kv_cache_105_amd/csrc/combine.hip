@@ -17,12 +17,16 @@
 
 namespace pkv {
 
+constexpr int kChunk = 1024;   // piece weights held in LDS at a time
+constexpr int kMaxStep = 4;    // output elements per lane: d_h <= 256 = 64 lanes x 4
+
 template <int D_STEP>
 __global__ __launch_bounds__(64) void combine_kernel(float* __restrict__ out,
                                                      const int32_t* __restrict__ context_lens,
                                                      const char* __restrict__ ws, int H_Q,
                                                      int H_KV, int d_h, int partition_tokens,
                                                      int max_parts) {
+  __shared__ float w_s[kChunk];
   const int hq = blockIdx.x, b = blockIdx.y, B = gridDim.y, lane = threadIdx.x;
   const WsHeader hd = *reinterpret_cast<const WsHeader*>(ws);
   float* dst = out + (static_cast<size_t>(b) * H_Q + hq) * d_h;
@@ -65,18 +69,23 @@ __global__ __launch_bounds__(64) void combine_kernel(float* __restrict__ out,
     return;
   }
 
-  // piece k -> partial index in the chosen layout
-  auto ml_at = [&](int k) -> const float* {
-    if (hd.mode == kWsPartition) return ml + 2 * k;
-    const int slot = (k == 0) ? first_slot : 0;
-    return ml + 2 * ((static_cast<size_t>(first_wave + k) * 2 + slot) * g + j);
-  };
-  auto o_at = [&](int k) -> const float* {
-    if (hd.mode == kWsPartition) return o + static_cast<size_t>(k) * d_h;
-    const int slot = (k == 0) ? first_slot : 0;
-    return o + ((static_cast<size_t>(first_wave + k) * 2 + slot) * g + j) * d_h;
-  };
+  // piece k -> its (m, l) pair and its o row in the chosen layout
+  size_t ml_step = 2, o_step = d_h;  // partition layout: pieces are contiguous
+  size_t ml_first = 0, o_first = 0;  // offset of piece 0 when it sits in another slot
+  if (hd.mode == kWsFlat) {
+    // piece k > 0 lives in slot 0 of wave first_wave + k; piece 0 in first_slot
+    const size_t base = (static_cast<size_t>(first_wave) * 2) * g + j;
+    ml += 2 * base;
+    o += base * d_h;
+    ml_step = 2 * 2 * static_cast<size_t>(g);
+    o_step = 2 * static_cast<size_t>(g) * d_h;
+    ml_first = 2 * static_cast<size_t>(first_slot) * g;
+    o_first = static_cast<size_t>(first_slot) * g * d_h;
+  }
+  auto ml_at = [&](int k) { return ml + k * ml_step + (k == 0 ? ml_first : 0); };
+  auto o_at = [&](int k) { return o + k * o_step + (k == 0 ? o_first : 0); };
 
+  // pass 1 (lane-parallel): M = max_k m_k and L = sum_k 2^(m_k - M) l_k
   float M = -INFINITY;
   for (int k = lane; k < P; k += 64) M = fmaxf(M, ml_at(k)[0]);
   for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
@@ -85,18 +94,51 @@ __global__ __launch_bounds__(64) void combine_kernel(float* __restrict__ out,
   for (int off = 32; off > 0; off >>= 1) Lsum += __shfl_xor(Lsum, off, 64);
   const float inv = 1.0f / Lsum;
 
-  for (int d0 = lane * D_STEP; d0 < d_h; d0 += 64 * D_STEP) {
-    float acc[D_STEP];
+  // pass 2: weights of up to kChunk pieces at a time in LDS, then every lane
+  // sums its output elements over the chunk with independent loads
+  constexpr int R = kMaxStep / D_STEP;  // element groups per lane (static: acc stays in VGPRs)
+  float acc[kMaxStep];
 #pragma unroll
-    for (int k = 0; k < D_STEP; ++k) acc[k] = 0.f;
-    for (int k = 0; k < P; ++k) {
-      const float w = exp2f(ml_at(k)[0] - M);
-      const float* src = o_at(k) + d0;
+  for (int e = 0; e < kMaxStep; ++e) acc[e] = 0.f;
+  const int d0 = lane * D_STEP;
+  for (int k0 = 0; k0 < P; k0 += kChunk) {
+    const int kn = min(kChunk, P - k0);
+    for (int k = lane; k < kn; k += 64) w_s[k] = exp2f(ml_at(k0 + k)[0] - M) * inv;
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the weights are in LDS
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
 #pragma unroll
-      for (int e = 0; e < D_STEP; ++e) acc[e] = fmaf(w, src[e], acc[e]);
+    for (int r = 0; r < R; ++r) {
+      const int d = d0 + r * 64 * D_STEP;
+      if (d >= d_h) continue;
+      int k = 0;
+      for (; k + 4 <= kn; k += 4) {
+        const float* s0 = o_at(k0 + k) + d;
+        const float* s1 = o_at(k0 + k + 1) + d;
+        const float* s2 = o_at(k0 + k + 2) + d;
+        const float* s3 = o_at(k0 + k + 3) + d;
+#pragma unroll
+        for (int e = 0; e < D_STEP; ++e) {
+          const float x0 = s0[e], x1 = s1[e], x2 = s2[e], x3 = s3[e];
+          acc[r * D_STEP + e] = fmaf(w_s[k], x0, acc[r * D_STEP + e]);
+          acc[r * D_STEP + e] = fmaf(w_s[k + 1], x1, acc[r * D_STEP + e]);
+          acc[r * D_STEP + e] = fmaf(w_s[k + 2], x2, acc[r * D_STEP + e]);
+          acc[r * D_STEP + e] = fmaf(w_s[k + 3], x3, acc[r * D_STEP + e]);
+        }
+      }
+      for (; k < kn; ++k) {
+        const float* s0 = o_at(k0 + k) + d;
+#pragma unroll
+        for (int e = 0; e < D_STEP; ++e) acc[r * D_STEP + e] = fmaf(w_s[k], s0[e], acc[r * D_STEP + e]);
+      }
     }
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);  // the next chunk rewrites w_s
+  }
 #pragma unroll
-    for (int e = 0; e < D_STEP; ++e) dst[d0 + e] = acc[e] * inv;
+  for (int r = 0; r < R; ++r) {
+    const int d = d0 + r * 64 * D_STEP;
+    if (d >= d_h) continue;
+#pragma unroll
+    for (int e = 0; e < D_STEP; ++e) dst[d + e] = acc[r * D_STEP + e];
   }
 }
 
