@@ -160,6 +160,8 @@ def main():
     ap.add_argument("--variant", type=int, default=0, help="0 auto, 1 generic, 2 mfma")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-blocks", type=int, default=0, metavar="N",
+                    help="also time pkv_copy_blocks on N random disjoint block pairs")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="after the bench, copy a MIB-sized buffer 5 times (plain copy kernel "
                          "of known size, to scale HBM counters)")
@@ -282,6 +284,30 @@ def main():
     ref["gather_gbs"] = gather_reference(w, pools, stream, args.steps)
     log(f"compute-free gather of the same tiles: {ref['gather_gbs']} GB/s "
         f"(partition kernel at {100 * achieved / ref['gather_gbs']:.1f}% of it)")
+
+    if args.copy_blocks > 0:
+        n = min(args.copy_blocks, w.num_blocks // 2)
+        gen = torch.Generator(device="cpu")
+        gen.manual_seed(11)
+        ids = torch.randperm(w.num_blocks, generator=gen)[:2 * n].to(torch.int32)
+        pairs = torch.stack([ids[:n], ids[n:]], dim=1).contiguous().to(dev)
+        for i in range(3):
+            kc, vc = pools[i % R][0]
+            pkv.copy_blocks(kc, vc, pairs, ks[0], vs[0], stream=stream)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for i in range(args.steps):
+            kc, vc = pools[i % R][0]
+            pkv.copy_blocks(kc, vc, pairs, ks[0], vs[0], stream=stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        cms = e0.elapsed_time(e1) / args.steps
+        blk = w.H_KV * w.block_size * w.d_h * metrics.DTYPE_BYTES[w.kv_dtype]
+        ref["copy_blocks_gbs"] = round(2 * 2 * n * blk / (cms * 1e-3) / 1e9, 1)
+        ref["copy_blocks_us"] = round(cms * 1e3, 2)
+        log(f"copy_blocks: {n} pairs x {blk} B x (K, V) in {cms * 1e3:.1f} us = "
+            f"{ref['copy_blocks_gbs']} GB/s read+write")
 
     if args.calibrate_copy > 0:
         src = torch.ones(args.calibrate_copy * 2 ** 20 // 4, dtype=torch.float32, device=dev)

@@ -126,8 +126,22 @@ int pkv_pool_free_queue(const pkv_pool* pool, int32_t* ids, int32_t cap, int32_t
 int pkv_seq_prepare_append(pkv_pool* pool, int32_t* table_row, int32_t max_blocks,
                            int32_t ctx_before, int32_t* n_blocks, int32_t* block_out,
                            int32_t* slot_out);
-/* Map the first n_full_blocks blocks of src_row into dst_row, one more
- * reference each (section 21.5 step 3).  BAD_BLOCK if any is not live. */
+/* Copy-on-write variant of pkv_seq_prepare_append (page 1 section 21.5, the
+ * paragraph after the walk: shared state is copied before a writer changes
+ * it, preserving the other requests' view).  When the target block is
+ * partly filled and shared (refcount > 1), a new block replaces it in this
+ * row, this row's reference moves from the shared block to the new one, and
+ * *cow_src receives the shared block: the caller must copy its contents into
+ * *block_out (pkv_copy_blocks, every layer) before appending.  Otherwise it
+ * behaves like pkv_seq_prepare_append and sets *cow_src = -1.
+ * OUT_OF_BLOCKS (and no change) if a copy is needed and no block is free. */
+int pkv_seq_prepare_append_cow(pkv_pool* pool, int32_t* table_row, int32_t max_blocks,
+                               int32_t ctx_before, int32_t* n_blocks, int32_t* block_out,
+                               int32_t* slot_out, int32_t* cow_src);
+/* Map the first n_blocks blocks of src_row into dst_row, one more reference
+ * each (section 21.5 step 3; sharing a partly filled last block makes the
+ * next writer of that block copy it, see above).  BAD_BLOCK if any is not
+ * live. */
 int pkv_seq_share_prefix(pkv_pool* pool, const int32_t* src_row, int32_t n_full_blocks,
                          int32_t* dst_row);
 /* Drop one reference to each of the n_blocks blocks (steps 4-5).  Checks
@@ -155,6 +169,16 @@ int pkv_kv_append(const void* k_new, const void* v_new, int in_dtype, void* k_ca
                   const int32_t* block_table, int32_t max_blocks_per_seq,
                   const int32_t* context_lens, int32_t B, int32_t H_KV, int32_t d_h,
                   int32_t block_size, int32_t num_blocks, pkv_stream_t stream);
+
+/* Block copies for copy-on-write (page 1 section 21.5): for each pair i of
+ * `pairs` (device int32 [n_pairs][2] = (src, dst)), every stored byte of
+ * physical block src -- all KV heads and slots of K and of V -- and, for
+ * FP8_E4M3 caches, its k/v scales are copied to block dst.  No block may
+ * appear in two pairs as a destination, or as both a source and a
+ * destination.  Pairs with an id outside [0, num_blocks) are skipped. */
+int pkv_copy_blocks(void* k_cache, void* v_cache, int kv_dtype, float* k_scale, float* v_scale,
+                    const int32_t* pairs, int32_t n_pairs, int32_t H_KV, int32_t d_h,
+                    int32_t block_size, int32_t num_blocks, pkv_stream_t stream);
 
 /* Work split (split-K) planning for paged_decode_attention.  The attention
  * kernels cut each request's positions into pieces whose partial results a

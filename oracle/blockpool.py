@@ -14,8 +14,9 @@ Table 21.1 and the five numbered steps after it:
   zero returns to the free pool at once (step 4, "immediate-release
   policy"), while a block still referenced stays live (step 4, block 7);
 * a shared block that is only partly filled must not be written in place
-  (copy-on-write paragraph after the walk); this model reports that case as
-  an error instead of copying.
+  (copy-on-write paragraph after the walk): ``prepare_append`` reports that
+  case as an error, ``prepare_append_cow`` moves the writer to a fresh block
+  and names the block whose contents must be copied into it.
 
 The free pool is a FIFO queue: ``alloc`` pops the head, a release pushes to
 the tail.  The pages call it a "free pool", a "free-block queue" (page 2) and
@@ -112,6 +113,26 @@ class BlockPool:
         if self.refcount[b] > 1:
             raise SharedBlock(f"block {b} is shared (refcount {self.refcount[b]})")
         return b, r
+
+    def prepare_append_cow(self, table_row: list, ctx_before: int) -> tuple:
+        """Like ``prepare_append``, but a shared target block is not refused:
+        the writer gets a private copy first (page 1, section 21.5, the
+        copy-on-write paragraph after the walk: shared state is copied before
+        a writer changes it, so the other requests keep their view).
+
+        Returns (physical block, slot, source block to copy or None).  The
+        new block is taken before the shared one loses this row's reference,
+        so an empty pool leaves everything unchanged."""
+        bs = self.block_size
+        j, r = divmod(ctx_before, bs)
+        if r == 0 or len(table_row) != j + 1 or self.refcount[table_row[j]] <= 1:
+            b, slot = self.prepare_append(table_row, ctx_before)
+            return b, slot, None
+        src = table_row[j]
+        dst = self.alloc()
+        self.decref(src)
+        table_row[j] = dst
+        return dst, r, src
 
     def share_prefix(self, src_row: list, n_full_blocks: int) -> list:
         """Map the first ``n_full_blocks`` complete blocks of ``src_row`` into

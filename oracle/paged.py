@@ -86,6 +86,23 @@ def append(k_cache, v_cache, kv_dtype: str, k_new, v_new, in_dtype: str,
     return kc, vc
 
 
+def copy_blocks(k_cache, v_cache, pairs, k_scale=None, v_scale=None):
+    """Copy-on-write block copies: block dst takes every stored byte (all KV
+    heads, all slots) and the scales of block src, for each (src, dst) pair.
+    Returns new arrays (the inputs are not modified)."""
+    kc = np.array(k_cache, copy=True)
+    vc = np.array(v_cache, copy=True)
+    ks = None if k_scale is None else np.array(k_scale, copy=True)
+    vs = None if v_scale is None else np.array(v_scale, copy=True)
+    for src, dst in pairs:
+        kc[dst] = k_cache[src]
+        vc[dst] = v_cache[src]
+        if ks is not None:
+            ks[dst] = k_scale[src]
+            vs[dst] = v_scale[src]
+    return kc, vc, ks, vs
+
+
 def decode_stored(pool_slice, kv_dtype: str, scale=None) -> np.ndarray:
     """Stored scalars -> float64 values (exact)."""
     if kv_dtype == F32:

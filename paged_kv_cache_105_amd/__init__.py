@@ -15,7 +15,7 @@ from . import _lib
 from ._lib import (PKV_BF16, PKV_F32, PKV_FP8_E4M3, PKV_VARIANT_AUTO, PKV_VARIANT_GENERIC,
                    PKV_VARIANT_MFMA, PKV_VARIANT_MFMA_PARTITION, PkvError, check, load)
 
-__all__ = ["kv_append", "decode_plan", "paged_decode_attention", "decode_partitions",
+__all__ = ["kv_append", "copy_blocks", "decode_plan", "paged_decode_attention", "decode_partitions",
            "combine_partitions", "set_decode_variant", "BlockPool", "PkvError", "load",
            "PKV_F32", "PKV_BF16", "PKV_FP8_E4M3", "PKV_VARIANT_AUTO", "PKV_VARIANT_GENERIC",
            "PKV_VARIANT_MFMA", "PKV_VARIANT_MFMA_PARTITION", "dtype_code"]
@@ -63,6 +63,14 @@ def kv_append(k_new, v_new, k_cache, v_cache, block_table, context_lens,
                                _ptr(v_scale), _ptr(block_table), block_table.shape[1],
                                _ptr(context_lens), B, H_KV, d_h, bs, num_blocks,
                                _stream(stream)), "pkv_kv_append")
+
+
+def copy_blocks(k_cache, v_cache, pairs, k_scale=None, v_scale=None, stream=None):
+    """pkv_copy_blocks: pairs is a device int32 tensor [n, 2] of (src, dst)."""
+    num_blocks, H_KV, bs, d_h = k_cache.shape
+    check(load().pkv_copy_blocks(_ptr(k_cache), _ptr(v_cache), _dtype_code(k_cache),
+                                 _ptr(k_scale), _ptr(v_scale), _ptr(pairs), pairs.shape[0], H_KV,
+                                 d_h, bs, num_blocks, _stream(stream)), "pkv_copy_blocks")
 
 
 def decode_plan(B, H_Q, H_KV, d_h, block_size, max_context_len, partition_tokens=0,
@@ -194,6 +202,16 @@ class BlockPool:
                                                C.byref(nb), C.byref(blk), C.byref(slot)),
               "pkv_seq_prepare_append")
         return nb.value, blk.value, slot.value
+
+    def prepare_append_cow(self, row, n_blocks: int, ctx_before: int):
+        """Returns (n_blocks_after, block, slot, cow_src); cow_src is -1 unless
+        a shared block had to be replaced by a private copy."""
+        nb, blk, slot, src = C.c_int32(n_blocks), C.c_int32(), C.c_int32(), C.c_int32()
+        check(self._lib.pkv_seq_prepare_append_cow(self._h, row, len(row), ctx_before,
+                                                   C.byref(nb), C.byref(blk), C.byref(slot),
+                                                   C.byref(src)),
+              "pkv_seq_prepare_append_cow")
+        return nb.value, blk.value, slot.value, src.value
 
     def share_prefix(self, src_row, n_full_blocks: int, dst_row):
         check(self._lib.pkv_seq_share_prefix(self._h, src_row, n_full_blocks, dst_row),

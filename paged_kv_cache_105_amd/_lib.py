@@ -39,10 +39,14 @@ SIGNATURES = {
     "pkv_pool_num_used": (C.c_int, [_vp, _pi32]),
     "pkv_pool_free_queue": (C.c_int, [_vp, _pi32, _i32, _pi32]),
     "pkv_seq_prepare_append": (C.c_int, [_vp, _pi32, _i32, _i32, _pi32, _pi32, _pi32]),
+    "pkv_seq_prepare_append_cow": (C.c_int, [_vp, _pi32, _i32, _i32, _pi32, _pi32, _pi32,
+                                             _pi32]),
     "pkv_seq_share_prefix": (C.c_int, [_vp, _pi32, _i32, _pi32]),
     "pkv_seq_release": (C.c_int, [_vp, _pi32, _i32]),
     "pkv_kv_append": (C.c_int, [_vp, _vp, C.c_int, _vp, _vp, C.c_int, _vp, _vp, _vp, _i32, _vp,
                                 _i32, _i32, _i32, _i32, _i32, _vp]),
+    "pkv_copy_blocks": (C.c_int, [_vp, _vp, C.c_int, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
+                                  _vp]),
     "pkv_decode_plan": (C.c_int, [_i32, _i32, _i32, _i32, _i32, _i32, _i32, C.c_int, C.c_int,
                                   _pi32, _pi32, C.POINTER(_sz)]),
     "pkv_paged_decode_attention": (C.c_int, [_vp, _vp, C.c_int, _vp, _vp, C.c_int, _vp, _vp,

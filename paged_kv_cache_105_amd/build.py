@@ -17,7 +17,8 @@ CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libpkv.so")
 BENCH_LIB = os.path.join(PKG, "libpkv_bench.so")   # measurement helper of bench.py
 
-HIP_SOURCES = ["kv_append.hip", "decode_generic.hip", "decode_mfma.hip", "combine.hip"]
+HIP_SOURCES = ["kv_append.hip", "copy_blocks.hip", "decode_generic.hip", "decode_mfma.hip",
+               "combine.hip"]
 CXX_SOURCES = ["api.cpp", "pool.cpp"]
 
 FLAGS = [

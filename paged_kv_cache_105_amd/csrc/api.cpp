@@ -28,6 +28,9 @@ bool mfma_supports(int q_dtype, int kv_dtype, int d_h, int block_size, int g);
 int mfma_flat_waves(int kv_dtype, int g, int depth, int B);
 hipError_t launch_decode_mfma(int kv_dtype, int depth, bool flat, int waves, const DecodeArgs& a,
                               hipStream_t stream);
+hipError_t launch_copy_blocks(void* k_cache, void* v_cache, float* k_scale, float* v_scale,
+                              const int32_t* pairs, int n_pairs, size_t block_bytes, int H_KV,
+                              int num_blocks, hipStream_t stream);
 hipError_t launch_combine(float* out, const int32_t* context_lens, const void* ws, int B, int H_Q,
                           int H_KV, int d_h, int partition_tokens, int max_parts,
                           hipStream_t stream);
@@ -239,6 +242,23 @@ int pkv_kv_append(const void* k_new, const void* v_new, int in_dtype, void* k_ca
                                           k_scale, v_scale, block_table, max_blocks_per_seq,
                                           context_lens, B, H_KV, d_h, block_size, num_blocks,
                                           static_cast<hipStream_t>(stream)));
+}
+
+int pkv_copy_blocks(void* k_cache, void* v_cache, int kv_dtype, float* k_scale, float* v_scale,
+                    const int32_t* pairs, int32_t n_pairs, int32_t H_KV, int32_t d_h,
+                    int32_t block_size, int32_t num_blocks, pkv_stream_t stream) {
+  if (!k_cache || !v_cache || !pairs || n_pairs < 0 || !valid_dtype(kv_dtype) || H_KV < 1 ||
+      d_h < 1 || d_h > kMaxDh || block_size < 1 || num_blocks < 1)
+    return PKV_ERR_INVALID_ARG;
+  if (kv_dtype == PKV_FP8_E4M3 && (!k_scale || !v_scale)) return PKV_ERR_INVALID_ARG;
+  if (n_pairs == 0) return PKV_OK;
+  if (n_pairs > 2147483647 / 2) return PKV_ERR_INVALID_ARG;
+  const size_t elem = kv_dtype == PKV_F32 ? 4 : (kv_dtype == PKV_BF16 ? 2 : 1);
+  const size_t block_bytes = static_cast<size_t>(H_KV) * block_size * d_h * elem;
+  return hip_status(pkv::launch_copy_blocks(
+      k_cache, v_cache, kv_dtype == PKV_FP8_E4M3 ? k_scale : nullptr,
+      kv_dtype == PKV_FP8_E4M3 ? v_scale : nullptr, pairs, n_pairs, block_bytes, H_KV,
+      num_blocks, static_cast<hipStream_t>(stream)));
 }
 
 int pkv_decode_plan(int32_t B, int32_t H_Q, int32_t H_KV, int32_t d_h, int32_t block_size,

@@ -147,6 +147,35 @@ int pkv_seq_prepare_append(pkv_pool* pool, int32_t* table_row, int32_t max_block
   return PKV_OK;
 }
 
+int pkv_seq_prepare_append_cow(pkv_pool* pool, int32_t* table_row, int32_t max_blocks,
+                               int32_t ctx_before, int32_t* n_blocks, int32_t* block_out,
+                               int32_t* slot_out, int32_t* cow_src) {
+  if (!cow_src) return PKV_ERR_INVALID_ARG;
+  *cow_src = -1;
+  if (pool && table_row && n_blocks && block_out && slot_out && ctx_before >= 0 &&
+      max_blocks > 0) {
+    const int32_t bs = pool->block_size;
+    const int32_t j = ctx_before / bs;
+    if (ctx_before % bs != 0 && *n_blocks == j + 1 && pool->live(table_row[j]) &&
+        pool->refcount[table_row[j]] > 1) {
+      // a writer into a shared, partly filled block gets a private copy: take
+      // the new block first so that an empty pool changes nothing
+      if (pool->count == 0) return PKV_ERR_OUT_OF_BLOCKS;
+      const int32_t src = table_row[j];
+      const int32_t dst = pool->pop();
+      pool->refcount[dst] = 1;
+      --pool->refcount[src];  // stays >= 1: other rows still hold it
+      table_row[j] = dst;
+      *cow_src = src;
+      *block_out = dst;
+      *slot_out = ctx_before % bs;
+      return PKV_OK;
+    }
+  }
+  return pkv_seq_prepare_append(pool, table_row, max_blocks, ctx_before, n_blocks, block_out,
+                                slot_out);
+}
+
 int pkv_seq_share_prefix(pkv_pool* pool, const int32_t* src_row, int32_t n_full_blocks,
                          int32_t* dst_row) {
   if (!pool || n_full_blocks < 0 || (n_full_blocks > 0 && (!src_row || !dst_row)))

@@ -110,3 +110,55 @@ def test_pool_walk_32gib_exhaustion_page_2():
         pool.alloc()
     with pytest.raises(blockpool.OutOfBlocks):
         pool.alloc()
+
+
+def test_copy_on_write_keeps_the_other_view():
+    # page 1, section 21.5, copy-on-write paragraph: C shares A's partly
+    # filled block 2 (2 of 4 slots); A's next write must go to a private copy
+    pool, rows = _initial_state()
+    c = pool.share_prefix(rows["A"], 2)
+    assert pool.refcount[2] == 2
+    with pytest.raises(blockpool.SharedBlock):
+        pool.prepare_append(list(rows["A"]), 6)
+    blk, slot, src = pool.prepare_append_cow(rows["A"], 6)
+    assert (blk, slot, src) == (5, 2, 2)          # the only free id of Table 21.1 is 5
+    assert rows["A"] == [7, 5] and c == [7, 2]
+    assert pool.refcount[2] == 1 and pool.refcount[5] == 1 and pool.refcount[7] == 2
+    # C, now the only holder of block 2, appends in place
+    assert pool.prepare_append_cow(c, 6) == (2, 2, None)
+    # a full pool refuses the copy and changes nothing
+    p2 = blockpool.BlockPool(2, 4)
+    r1 = []
+    for pos in range(2):
+        p2.prepare_append(r1, pos)
+    r2 = p2.share_prefix(r1, 1)
+    p2.alloc()
+    with pytest.raises(blockpool.OutOfBlocks):
+        p2.prepare_append_cow(r1, 2)
+    assert r1 == r2 and p2.refcount[r1[0]] == 2
+
+
+def test_copy_on_write_data_flow():
+    # the copy preserves every earlier position of both requests, and only the
+    # writer sees its new token
+    import numpy as np
+
+    from oracle import paged
+    rng = np.random.default_rng(0)
+    pool = blockpool.BlockPool(8, 4)
+    a = []
+    for pos in range(6):
+        pool.prepare_append(a, pos)
+    c = pool.share_prefix(a, 2)
+    kc = rng.standard_normal((8, 1, 4, 2)).astype(np.float32)
+    vc = rng.standard_normal((8, 1, 4, 2)).astype(np.float32)
+    before_a = paged.gather_head(kc, "f32", None, a, 6, 0, 4)
+    blk, slot, src = pool.prepare_append_cow(a, 6)
+    kc, vc, _, _ = paged.copy_blocks(kc, vc, [(src, blk)])
+    new = np.full((1, 1, 2), 9.0, dtype=np.float32)
+    kc, vc = paged.append(kc, vc, "f32", new, new, "f32", np.array([a]), np.array([7]), 4)
+    after_a = paged.gather_head(kc, "f32", None, a, 7, 0, 4)
+    after_c = paged.gather_head(kc, "f32", None, c, 6, 0, 4)
+    assert np.array_equal(after_a[:6], before_a)
+    assert np.array_equal(after_a[6], [9.0, 9.0])
+    assert np.array_equal(after_c, before_a)
