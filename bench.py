@@ -108,6 +108,52 @@ def gather_reference(w, pools, stream, steps, waves=2048):
     return round(nbytes / (ms[1] * 1e-3) / 1e9, 1)
 
 
+def host_prefix_identity(block_size: int, prompt_tokens: int = 32768, reps: int = 20):
+    """Host cost of prefix reuse for one long prompt: chained block identities
+    (the library's SHA-256), a full match against a pool that holds them as
+    idle cached blocks (each block leaves the free queue) and the release that
+    puts them back.  For scale, the same chain through Python's hashlib
+    (OpenSSL) is timed too."""
+    import ctypes as C
+
+    import numpy as np
+    rng = np.random.default_rng(11)
+    toks = rng.integers(0, 128_000, prompt_tokens).astype(np.int32)
+    h0 = pkv.prefix_root(b"bench;bf16")
+    nblk = prompt_tokens // block_size
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        hs = pkv.block_hashes(h0, toks, block_size)
+    hash_us = (time.perf_counter() - t0) * 1e6 / reps
+    pool = pkv.BlockPool(4 * nblk, block_size)
+    row = (C.c_int32 * nblk)()
+    n = 0
+    for _ in range(nblk):
+        n, _, _ = pool.prepare_append(row, n, n * block_size)
+    pool.cache_blocks(row, n, nblk * block_size, hs)
+    pool.release(row, n)
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        hit = pool.match_prefix(hs, row)
+        pool.release(row, hit)
+    match_us = (time.perf_counter() - t0) * 1e6 / reps
+    if hit != nblk:
+        raise RuntimeError(f"prefix match found {hit} of {nblk} blocks")
+    raw = toks.astype("<i4").tobytes()
+    step = 4 * block_size
+    t0 = time.perf_counter()
+    h = h0
+    for j in range(nblk):
+        h = hashlib.sha256(h + raw[j * step:(j + 1) * step]).digest()
+    openssl_us = (time.perf_counter() - t0) * 1e6
+    if h != hs[-32:]:
+        raise RuntimeError("library block identities differ from hashlib's")
+    return {"prompt_tokens": prompt_tokens, "blocks": nblk,
+            "hash_us": round(hash_us, 1), "hash_blocks_per_s": round(nblk / hash_us * 1e6),
+            "match_and_release_us": round(match_us, 1),
+            "hashlib_chain_us": round(openssl_us, 1)}
+
+
 def cpu_baseline(w, layer_tensors, budget_s: float):
     """Time the oracle (as it stands) on a bounded sample: the append of the
     whole batch, then attention request by request until ~budget_s."""
@@ -354,6 +400,7 @@ def main():
                      "algorithmic_bytes_per_launch": att["total"],
                      "avg_launch_us": round(kern_avg_ms * 1e3, 3)},
         "cpu_baseline": cpu,
+        "host_prefix_identity": host_prefix_identity(w.block_size),
     }
     print(json.dumps(res), flush=True)
 

@@ -150,6 +150,67 @@ int pkv_seq_share_prefix(pkv_pool* pool, const int32_t* src_row, int32_t n_full_
 int pkv_seq_release(pkv_pool* pool, const int32_t* table_row, int32_t n_blocks);
 
 /* ------------------------------------------------------------------------
+ * Prefix identity and retention (page 1 section 21.4, the chained block
+ * identities h_i = hash(h_{i-1}, tokens_i), and section 21.5 step 5; page 2
+ * "KV Cache Explained", sections "Why PagedAttention allocates KV in
+ * blocks", "Follow the 32 GiB pool until it cannot allocate one more block"
+ * and "Cache identity is a correctness boundary").
+ *
+ * An identity is a 32-byte SHA-256 digest (FIPS 180-4):
+ *   h_0 = SHA-256(identity bytes of the configuration and isolation salt)
+ *   h_i = SHA-256(h_{i-1} || tokens of block i as little-endian int32)
+ * Only complete blocks have an identity.
+ *
+ * A block of the pool may hold one identity; the pool maps each identity it
+ * holds to one block.  A block keeps its identity after its last reference
+ * and joins the free queue tail like any other block ("cached" is not
+ * "pinned"); the queue order is therefore the eviction order.  When alloc
+ * (or a prepare_append that opens a block, or a copy-on-write) takes a
+ * block that still holds an identity, the identity is dropped (an eviction).
+ * Blocks without identities behave exactly as in the plain pool above.
+ * ---------------------------------------------------------------------- */
+#define PKV_DIGEST_BYTES 32
+
+/* out[32] = h_0 = SHA-256 of the n identity bytes.  The bytes should name
+ * everything that makes cached K/V interchangeable (model revision,
+ * adapter, position settings, cache dtype and layout, isolation salt). */
+int pkv_prefix_root(const void* identity, size_t n, uint8_t* out);
+/* Identities of the n_tokens / block_size complete blocks of `tokens`
+ * (token ids), chained from `parent` (h_0, or the identity of the block
+ * before the first one given).  out: [cap_blocks][32]; *n_out receives the
+ * number of complete blocks.  INVALID_ARG (nothing written) if cap_blocks is
+ * smaller than that.  A trailing partial block gets no identity. */
+int pkv_block_hashes(const uint8_t* parent, const int32_t* tokens, int64_t n_tokens,
+                     int32_t block_size, uint8_t* out, int64_t cap_blocks, int64_t* n_out);
+/* Block that holds `digest`, or -1 in *block_id.  Changes nothing. */
+int pkv_pool_lookup(const pkv_pool* pool, const uint8_t* digest, int32_t* block_id);
+/* Start a request's table row from retained blocks: for j = 0, 1, ...
+ * while j < min(n_hashes, max_blocks) and hashes[j] (of [n_hashes][32]) is
+ * held by a block, take one reference on that block (an idle cached block
+ * leaves the free queue) and write it to table_row[j].  Stops at the first
+ * identity not held.  *n_hit receives the number of blocks matched, which
+ * is the row's new block count; the caller continues with
+ * pkv_seq_prepare_append from position n_hit * block_size.  Counts
+ * n_hashes identities asked for and n_hit reused in the statistics. */
+int pkv_pool_match_prefix(pkv_pool* pool, const uint8_t* hashes, int32_t n_hashes,
+                          int32_t* table_row, int32_t max_blocks, int32_t* n_hit);
+/* Give the complete blocks of a row their identities: for j <
+ * min(n_hashes, ctx_len / block_size, n_blocks), block table_row[j] gets
+ * hashes[j] unless it already holds it, or another block already holds
+ * that identity (the block then stays without one).  *n_cached receives the
+ * number of blocks that got an identity.  BAD_BLOCK if one of those blocks
+ * is not live; INVALID_ARG if one already holds a different identity (a
+ * complete block's contents do not change).  Both checks run first, and a
+ * failed check changes nothing. */
+int pkv_pool_cache_blocks(pkv_pool* pool, const int32_t* table_row, int32_t n_blocks,
+                          int32_t ctx_len, const uint8_t* hashes, int32_t n_hashes,
+                          int32_t* n_cached);
+/* stats[5] = { identities asked for by match_prefix, blocks reused,
+ * identities evicted, free blocks that hold an identity, blocks that hold
+ * an identity }. */
+int pkv_pool_prefix_stats(const pkv_pool* pool, int64_t* stats);
+
+/* ------------------------------------------------------------------------
  * Device entry points
  * ---------------------------------------------------------------------- */
 

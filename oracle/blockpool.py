@@ -21,6 +21,26 @@ Table 21.1 and the five numbered steps after it:
 The free pool is a FIFO queue: ``alloc`` pops the head, a release pushes to
 the tail.  The pages call it a "free pool", a "free-block queue" (page 2) and
 a "free list" (page 3) without fixing an order; FIFO is the plain reading.
+
+Prefix retention (page 1 section 21.5 step 5, and the exercise answer at the
+end of that chapter: after its last reference a block is either kept as an
+evictable prefix entry or freed; page 2 "KV Cache Explained", sections "Why
+PagedAttention allocates KV in blocks" and "Follow the 32 GiB pool until it
+cannot allocate one more block": a free-block queue plus a hash-to-block
+lookup; a cached block with no running reference stays available for
+eviction; allocation uses empty blocks first and then reclaims the oldest
+idle cached ones):
+
+* ``cache_blocks`` gives complete blocks of a row their identity
+  (``oracle.prefix``); an identity already held by another block leaves the
+  new block without one;
+* a block whose count reaches zero keeps its identity and joins the queue
+  tail like any other free block, so the queue order is the eviction order;
+* ``alloc`` pops the head; if that block has an identity the identity is
+  dropped (an eviction);
+* ``match_prefix`` takes a reference on the block of each leading identity
+  that is present, stopping at the first one that is not; a hit on a block
+  in the queue takes it out of the queue.
 """
 
 from __future__ import annotations
@@ -62,12 +82,20 @@ class BlockPool:
         self.block_size = block_size
         self.free = deque(free_order)
         self.refcount = [0] * num_blocks
+        self.hash_of = {}        # block -> identity
+        self.block_of = {}       # identity -> block
+        self.queried = 0         # identities asked for by match_prefix
+        self.hits = 0            # of those, blocks reused
+        self.evictions = 0       # identities dropped by alloc
 
     # ---- block level -----------------------------------------------------
     def alloc(self) -> int:
         if not self.free:
             raise OutOfBlocks("no free block")
         b = self.free.popleft()
+        if b in self.hash_of:
+            del self.block_of[self.hash_of.pop(b)]
+            self.evictions += 1
         self.refcount[b] = 1
         return b
 
@@ -90,6 +118,13 @@ class BlockPool:
 
     def num_used(self) -> int:
         return self.num_blocks - len(self.free)
+
+    def num_cached_idle(self) -> int:
+        """Free blocks that still hold an identity (evictable prefix entries)."""
+        return sum(1 for b in self.hash_of if self.refcount[b] == 0)
+
+    def lookup(self, h: bytes):
+        return self.block_of.get(bytes(h))
 
     # ---- sequence level --------------------------------------------------
     def prepare_append(self, table_row: list, ctx_before: int) -> tuple:
@@ -150,3 +185,43 @@ class BlockPool:
         section 21.5, steps 4 and 5)."""
         for b in table_row:
             self.decref(b)
+
+    # ---- prefix retention ------------------------------------------------
+    def match_prefix(self, hashes) -> list:
+        """Reuse the longest run of leading identities that are present: one
+        more reference on each matched block, a queued block leaves the queue.
+        Returns the new table row (the matched blocks, in order)."""
+        row = []
+        for h in hashes:
+            b = self.block_of.get(bytes(h))
+            if b is None:
+                break
+            if self.refcount[b] == 0:
+                self.free.remove(b)
+            self.refcount[b] += 1
+            row.append(b)
+        self.queried += len(hashes)
+        self.hits += len(row)
+        return row
+
+    def cache_blocks(self, table_row: list, ctx_len: int, hashes) -> int:
+        """Give the complete blocks of a row (the first ctx_len // block_size,
+        at most len(hashes)) their identities.  Returns how many blocks got a
+        new identity.  A block that already has a different identity is an
+        error (a complete block's contents do not change); checks happen
+        before any change."""
+        n = min(len(hashes), ctx_len // self.block_size, len(table_row))
+        for j in range(n):
+            b = table_row[j]
+            self._check(b)
+            if b in self.hash_of and self.hash_of[b] != bytes(hashes[j]):
+                raise InvalidArg(f"block {b} already holds another identity")
+        added = 0
+        for j in range(n):
+            b, h = table_row[j], bytes(hashes[j])
+            if b in self.hash_of or h in self.block_of:
+                continue
+            self.hash_of[b] = h
+            self.block_of[h] = b
+            added += 1
+        return added

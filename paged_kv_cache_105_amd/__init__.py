@@ -17,8 +17,40 @@ from ._lib import (PKV_BF16, PKV_F32, PKV_FP8_E4M3, PKV_VARIANT_AUTO, PKV_VARIAN
 
 __all__ = ["kv_append", "copy_blocks", "decode_plan", "paged_decode_attention", "decode_partitions",
            "combine_partitions", "set_decode_variant", "BlockPool", "PkvError", "load",
+           "prefix_root", "block_hashes", "DIGEST_BYTES",
            "PKV_F32", "PKV_BF16", "PKV_FP8_E4M3", "PKV_VARIANT_AUTO", "PKV_VARIANT_GENERIC",
            "PKV_VARIANT_MFMA", "PKV_VARIANT_MFMA_PARTITION", "dtype_code"]
+
+
+DIGEST_BYTES = _lib.PKV_DIGEST_BYTES
+
+
+def prefix_root(identity: bytes) -> bytes:
+    """h_0: SHA-256 of the configuration / isolation identity bytes
+    (pkv_prefix_root)."""
+    lib = load()
+    identity = bytes(identity)
+    out = (C.c_uint8 * DIGEST_BYTES)()
+    check(lib.pkv_prefix_root(identity, len(identity), out), "pkv_prefix_root")
+    return bytes(out)
+
+
+def block_hashes(parent: bytes, tokens, block_size: int) -> bytes:
+    """Chained identities of the complete blocks of ``tokens`` (an int32
+    sequence or numpy array), as one bytes object of 32 bytes per block
+    (pkv_block_hashes)."""
+    import numpy as np
+    lib = load()
+    toks = np.ascontiguousarray(np.asarray(tokens, dtype=np.int32))
+    parent = bytes(parent)
+    if len(parent) != DIGEST_BYTES:
+        raise PkvError(-1, "pkv_block_hashes")
+    nb = len(toks) // block_size if block_size > 0 else 0
+    out = (C.c_uint8 * max(1, nb * DIGEST_BYTES))()
+    n = C.c_int64()
+    check(lib.pkv_block_hashes(parent, toks.ctypes.data_as(C.POINTER(C.c_int32)), len(toks),
+                               block_size, out, nb, C.byref(n)), "pkv_block_hashes")
+    return bytes(out)[:n.value * DIGEST_BYTES]
 
 
 def dtype_code(t) -> int:
@@ -219,3 +251,32 @@ class BlockPool:
 
     def release(self, row, n_blocks: int):
         check(self._lib.pkv_seq_release(self._h, row, n_blocks), "pkv_seq_release")
+
+    # ---- prefix identity and retention ------------------------------------
+    def lookup(self, digest: bytes) -> int:
+        b = C.c_int32()
+        check(self._lib.pkv_pool_lookup(self._h, bytes(digest), C.byref(b)), "pkv_pool_lookup")
+        return b.value
+
+    def match_prefix(self, hashes: bytes, row) -> int:
+        """hashes: concatenated 32-byte identities; row: ctypes int32 array
+        (the new request's table row).  Returns the number of blocks matched."""
+        hashes = bytes(hashes)
+        n = C.c_int32()
+        check(self._lib.pkv_pool_match_prefix(self._h, hashes, len(hashes) // DIGEST_BYTES, row,
+                                              len(row), C.byref(n)), "pkv_pool_match_prefix")
+        return n.value
+
+    def cache_blocks(self, row, n_blocks: int, ctx_len: int, hashes: bytes) -> int:
+        hashes = bytes(hashes)
+        n = C.c_int32()
+        check(self._lib.pkv_pool_cache_blocks(self._h, row, n_blocks, ctx_len, hashes,
+                                              len(hashes) // DIGEST_BYTES, C.byref(n)),
+              "pkv_pool_cache_blocks")
+        return n.value
+
+    def prefix_stats(self) -> dict:
+        st = (C.c_int64 * 5)()
+        check(self._lib.pkv_pool_prefix_stats(self._h, st), "pkv_pool_prefix_stats")
+        return dict(queried=st[0], hits=st[1], evictions=st[2], cached_idle=st[3],
+                    hashed=st[4])

@@ -17,6 +17,7 @@ PKV_OK = 0
 STATUS_NAMES = {0: "ok", -1: "invalid_arg", -2: "out_of_blocks", -3: "bad_block",
                 -4: "shared_block", -5: "hip", -6: "workspace", -7: "unsupported"}
 PKV_F32, PKV_BF16, PKV_FP8_E4M3 = 0, 1, 2
+PKV_DIGEST_BYTES = 32
 PKV_VARIANT_AUTO, PKV_VARIANT_GENERIC, PKV_VARIANT_MFMA, PKV_VARIANT_MFMA_PARTITION = 0, 1, 2, 3
 
 _i32 = C.c_int32
@@ -43,6 +44,13 @@ SIGNATURES = {
                                              _pi32]),
     "pkv_seq_share_prefix": (C.c_int, [_vp, _pi32, _i32, _pi32]),
     "pkv_seq_release": (C.c_int, [_vp, _pi32, _i32]),
+    "pkv_prefix_root": (C.c_int, [_vp, _sz, _vp]),
+    "pkv_block_hashes": (C.c_int, [_vp, _pi32, C.c_int64, _i32, _vp, C.c_int64,
+                                   C.POINTER(C.c_int64)]),
+    "pkv_pool_lookup": (C.c_int, [_vp, _vp, _pi32]),
+    "pkv_pool_match_prefix": (C.c_int, [_vp, _vp, _i32, _pi32, _i32, _pi32]),
+    "pkv_pool_cache_blocks": (C.c_int, [_vp, _pi32, _i32, _i32, _vp, _i32, _pi32]),
+    "pkv_pool_prefix_stats": (C.c_int, [_vp, C.POINTER(C.c_int64)]),
     "pkv_kv_append": (C.c_int, [_vp, _vp, C.c_int, _vp, _vp, C.c_int, _vp, _vp, _vp, _i32, _vp,
                                 _i32, _i32, _i32, _i32, _i32, _vp]),
     "pkv_copy_blocks": (C.c_int, [_vp, _vp, C.c_int, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,

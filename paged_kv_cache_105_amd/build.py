@@ -19,7 +19,7 @@ BENCH_LIB = os.path.join(PKG, "libpkv_bench.so")   # measurement helper of bench
 
 HIP_SOURCES = ["kv_append.hip", "copy_blocks.hip", "decode_generic.hip", "decode_mfma.hip",
                "combine.hip"]
-CXX_SOURCES = ["api.cpp", "pool.cpp"]
+CXX_SOURCES = ["api.cpp", "pool.cpp", "sha256.cpp"]
 
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
