@@ -117,6 +117,8 @@ def host_prefix_identity(block_size: int, prompt_tokens: int = 32768, reps: int 
     import ctypes as C
 
     import numpy as np
+
+    import paged_kv_cache_105_amd as pkv
     rng = np.random.default_rng(11)
     toks = rng.integers(0, 128_000, prompt_tokens).astype(np.int32)
     h0 = pkv.prefix_root(b"bench;bf16")

@@ -343,6 +343,9 @@ int pkv_combine_partitions(float* out, const int32_t* context_lens, int32_t max_
     return PKV_ERR_INVALID_ARG;
   // without a workspace no partial can exist: the partition call wrote out
   if (!workspace || workspace_bytes < pkv::kWsHeader) return PKV_OK;
+  // the combine reads and writes 16-byte vectors
+  if ((reinterpret_cast<uintptr_t>(workspace) | reinterpret_cast<uintptr_t>(out)) & 15)
+    return PKV_ERR_INVALID_ARG;
   const int pt = resolve_partition(B, H_KV, block_size, max_context_len, partition_tokens);
   if (pt % block_size) return PKV_ERR_INVALID_ARG;
   const int max_parts = (max_context_len + pt - 1) / pt;

@@ -12,33 +12,66 @@
 // One wave per (query head, request).  The workspace header says which
 // layout the partition kernel wrote (see pkv_device.h).  Requests whose
 // result the partition kernel wrote directly are skipped.
+//
+// The kernel is latency bound (a few KiB per wave), so it is organised to
+// keep the number of dependent memory round trips small: each lane loads
+// the (m, l) pair of one piece at a time and merges them into its own
+// running pair, one wave reduction gives (M, L), the weights stay in the
+// lanes that computed them and are read with a lane shuffle, and the o rows
+// are read as VW-wide vectors, several pieces per wave instruction, with
+// kUnroll loads issued before any of them is used.
 
 #include "pkv_device.h"
 
 namespace pkv {
 
-constexpr int kChunk = 1024;   // piece weights held in LDS at a time
-constexpr int kMaxStep = 4;    // output elements per lane: d_h <= 256 = 64 lanes x 4
+namespace {
 
-template <int D_STEP>
+constexpr int kUnroll = 8;
+
+template <int VW>
+struct VecT;
+template <>
+struct VecT<1> {
+  using type = float;
+};
+template <>
+struct VecT<4> {
+  typedef float type __attribute__((ext_vector_type(4)));
+};
+
+// merge (m2, l2) into (m, l): both are (max, sum of 2^(s - max)) of a set
+__device__ inline void lse_merge(float& m, float& l, float m2, float l2) {
+  const float mn = fmaxf(m, m2);
+  const float a = (m == mn) ? 1.f : exp2f(m - mn);     // also covers m = m2 = -inf
+  const float b = (m2 == mn) ? 1.f : exp2f(m2 - mn);
+  l = l * a + l2 * b;
+  m = mn;
+}
+
+}  // namespace
+
+// VW: floats per vector load (4 when d_h % 4 == 0, else 1).  R: vector
+// columns per lane when a row has more than 64 of them (only VW = 1).
+template <int VW, int R>
 __global__ __launch_bounds__(64) void combine_kernel(float* __restrict__ out,
                                                      const int32_t* __restrict__ context_lens,
                                                      const char* __restrict__ ws, int H_Q,
                                                      int H_KV, int d_h, int partition_tokens,
                                                      int max_parts) {
-  __shared__ float w_s[kChunk];
+  using Vec = typename VecT<VW>::type;
+  __shared__ Vec red_s[64 * R];
   const int hq = blockIdx.x, b = blockIdx.y, B = gridDim.y, lane = threadIdx.x;
   const WsHeader hd = *reinterpret_cast<const WsHeader*>(ws);
   float* dst = out + (static_cast<size_t>(b) * H_Q + hq) * d_h;
 
   // Locate the pieces: piece k (k < P) has its (m, l) at ml + k * ml_step
-  // and its o at o + k * o_step, after a per-piece base offset.
+  // and its o at o + k * o_step, piece 0 shifted by (ml_first, o_first).
   int P = 0;
   const float* ml = nullptr;
   const float* o = nullptr;
-  // flat layout: pieces come from consecutive waves, each in slot 0 except
-  // the first wave's piece when that wave started in an earlier sequence
-  int first_wave = 0, first_slot = 0, g = 1, j = 0;
+  size_t ml_step = 2, o_step = d_h;  // partition layout: pieces are contiguous
+  size_t ml_first = 0, o_first = 0;
   if (hd.mode == kWsPartition) {
     const int n = context_lens[b];
     P = min((n + partition_tokens - 1) / partition_tokens, max_parts);
@@ -48,97 +81,108 @@ __global__ __launch_bounds__(64) void combine_kernel(float* __restrict__ out,
     ml = reinterpret_cast<const float*>(ws + PL.ml) + 2 * base;
     o = reinterpret_cast<const float*>(ws + PL.o) + base * d_h;
   } else if (hd.mode == kWsFlat) {
-    const int W = hd.waves, C = hd.chunks;
-    g = hd.g;
-    const int h = hq / g;
-    j = hq % g;
+    // flat layout: pieces come from consecutive waves, each in slot 0 except
+    // the first wave's piece when that wave started in an earlier sequence
+    const int W = hd.waves, C = hd.chunks, g = hd.g;
+    const int h = hq / g, j = hq % g;
     const FlatLayout FL = flat_layout(B, W, g, d_h);
     const int32_t* prefix = reinterpret_cast<const int32_t*>(ws + FL.prefix);
     const int nb = prefix[b + 1] - prefix[b];
     if (nb <= 0) return;
     const long long T = static_cast<long long>(H_KV) * prefix[B];
     const long long S = static_cast<long long>(H_KV) * prefix[b] + static_cast<long long>(h) * nb;
-    first_wave = flat_wave_of(S, T, C);
+    const int first_wave = flat_wave_of(S, T, C);
     const int last_wave = flat_wave_of(S + nb - 1, T, C);
     if (first_wave == last_wave) return;  // written final by its wave
-    first_slot = flat_chunk_lo(first_wave, T, C) == S ? 0 : 1;
+    const int first_slot = flat_chunk_lo(first_wave, T, C) == S ? 0 : 1;
     P = last_wave - first_wave + 1;
-    ml = reinterpret_cast<const float*>(ws + FL.ml);
-    o = reinterpret_cast<const float*>(ws + FL.o);
-  } else {
-    return;
-  }
-
-  // piece k -> its (m, l) pair and its o row in the chosen layout
-  size_t ml_step = 2, o_step = d_h;  // partition layout: pieces are contiguous
-  size_t ml_first = 0, o_first = 0;  // offset of piece 0 when it sits in another slot
-  if (hd.mode == kWsFlat) {
-    // piece k > 0 lives in slot 0 of wave first_wave + k; piece 0 in first_slot
     const size_t base = (static_cast<size_t>(first_wave) * 2) * g + j;
-    ml += 2 * base;
-    o += base * d_h;
+    ml = reinterpret_cast<const float*>(ws + FL.ml) + 2 * base;
+    o = reinterpret_cast<const float*>(ws + FL.o) + base * d_h;
     ml_step = 2 * 2 * static_cast<size_t>(g);
     o_step = 2 * static_cast<size_t>(g) * d_h;
     ml_first = 2 * static_cast<size_t>(first_slot) * g;
     o_first = static_cast<size_t>(first_slot) * g * d_h;
+  } else {
+    return;
   }
   auto ml_at = [&](int k) { return ml + k * ml_step + (k == 0 ? ml_first : 0); };
   auto o_at = [&](int k) { return o + k * o_step + (k == 0 ? o_first : 0); };
 
-  // pass 1 (lane-parallel): M = max_k m_k and L = sum_k 2^(m_k - M) l_k
-  float M = -INFINITY;
-  for (int k = lane; k < P; k += 64) M = fmaxf(M, ml_at(k)[0]);
-  for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
-  float Lsum = 0.f;
-  for (int k = lane; k < P; k += 64) Lsum = fmaf(exp2f(ml_at(k)[0] - M), ml_at(k)[1], Lsum);
-  for (int off = 32; off > 0; off >>= 1) Lsum += __shfl_xor(Lsum, off, 64);
-  const float inv = 1.0f / Lsum;
+  // pass 1: every lane merges the pieces lane, lane + 64, ... into its own
+  // (m, l); the first chunk's m stays in a register for pass 2
+  float m_own = -INFINITY, m_lane = -INFINITY, l_lane = 0.f;
+  if (lane < P) {
+    const float2 x = *reinterpret_cast<const float2*>(ml_at(lane));
+    m_own = m_lane = x.x;
+    l_lane = x.y;
+  }
+  for (int k = lane + 64; k < P; k += 64) {
+    const float2 x = *reinterpret_cast<const float2*>(ml_at(k));
+    lse_merge(m_lane, l_lane, x.x, x.y);
+  }
+  for (int off = 32; off > 0; off >>= 1) {
+    const float m2 = __shfl_xor(m_lane, off, 64), l2 = __shfl_xor(l_lane, off, 64);
+    lse_merge(m_lane, l_lane, m2, l2);
+  }
+  const float M = m_lane, inv = 1.0f / l_lane;
 
-  // pass 2: weights of up to kChunk pieces at a time in LDS, then every lane
-  // sums its output elements over the chunk with independent loads
-  constexpr int R = kMaxStep / D_STEP;  // element groups per lane (static: acc stays in VGPRs)
-  float acc[kMaxStep];
+  // pass 2: lanes are split into PPI groups of LP lanes; group s reads piece
+  // i * PPI + s of the chunk on iteration i, lane c of a group reads vector
+  // columns c, c + 64, ... of that piece's row
+  const int ncol = d_h / VW;
+  const int LP = ncol < 64 ? ncol : 64;
+  const int PPI = 64 / LP;
+  const int sub = lane / LP, c = lane % LP;
+  const bool on = sub < PPI;
+  Vec acc[R];
 #pragma unroll
-  for (int e = 0; e < kMaxStep; ++e) acc[e] = 0.f;
-  const int d0 = lane * D_STEP;
-  for (int k0 = 0; k0 < P; k0 += kChunk) {
-    const int kn = min(kChunk, P - k0);
-    for (int k = lane; k < kn; k += 64) w_s[k] = exp2f(ml_at(k0 + k)[0] - M) * inv;
-    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the weights are in LDS
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  for (int r = 0; r < R; ++r) acc[r] = Vec(0.f);
+  for (int k0 = 0; k0 < P; k0 += 64) {
+    const int kn = min(64, P - k0);
+    const float mk = (k0 == 0) ? m_own : (lane < kn ? ml_at(k0 + lane)[0] : -INFINITY);
+    const float w = lane < kn ? exp2f(mk - M) * inv : 0.f;
+    const int iters = (kn + PPI - 1) / PPI;
+    for (int i0 = 0; i0 < iters; i0 += kUnroll) {
+      Vec x[kUnroll][R];
+      float wk[kUnroll];
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const int kk = (i0 + u) * PPI + sub;     // piece within the chunk
+        const bool valid = on && kk < kn;
+        wk[u] = __shfl(w, valid ? kk : 0, 64);
+        const Vec* row = reinterpret_cast<const Vec*>(o_at(k0 + (valid ? kk : 0)));
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          const int col = c + r * 64;
+          x[u][r] = (valid && col < ncol) ? row[col] : Vec(0.f);
+        }
+        if (!valid) wk[u] = 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u)
+#pragma unroll
+        for (int r = 0; r < R; ++r) acc[r] += wk[u] * x[u][r];
+    }
+  }
+
+  // sum the PPI groups' partial rows
+  if (PPI > 1) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) red_s[lane + 64 * r] = acc[r];
+    __syncthreads();
+    if (sub == 0) {
+      for (int s = 1; s < PPI; ++s)
+#pragma unroll
+        for (int r = 0; r < R; ++r) acc[r] += red_s[s * LP + c + 64 * r];
+    }
+  }
+  if (sub == 0) {
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      const int d = d0 + r * 64 * D_STEP;
-      if (d >= d_h) continue;
-      int k = 0;
-      for (; k + 4 <= kn; k += 4) {
-        const float* s0 = o_at(k0 + k) + d;
-        const float* s1 = o_at(k0 + k + 1) + d;
-        const float* s2 = o_at(k0 + k + 2) + d;
-        const float* s3 = o_at(k0 + k + 3) + d;
-#pragma unroll
-        for (int e = 0; e < D_STEP; ++e) {
-          const float x0 = s0[e], x1 = s1[e], x2 = s2[e], x3 = s3[e];
-          acc[r * D_STEP + e] = fmaf(w_s[k], x0, acc[r * D_STEP + e]);
-          acc[r * D_STEP + e] = fmaf(w_s[k + 1], x1, acc[r * D_STEP + e]);
-          acc[r * D_STEP + e] = fmaf(w_s[k + 2], x2, acc[r * D_STEP + e]);
-          acc[r * D_STEP + e] = fmaf(w_s[k + 3], x3, acc[r * D_STEP + e]);
-        }
-      }
-      for (; k < kn; ++k) {
-        const float* s0 = o_at(k0 + k) + d;
-#pragma unroll
-        for (int e = 0; e < D_STEP; ++e) acc[r * D_STEP + e] = fmaf(w_s[k], s0[e], acc[r * D_STEP + e]);
-      }
+      const int col = c + r * 64;
+      if (col < ncol) reinterpret_cast<Vec*>(dst)[col] = acc[r];
     }
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);  // the next chunk rewrites w_s
-  }
-#pragma unroll
-  for (int r = 0; r < R; ++r) {
-    const int d = d0 + r * 64 * D_STEP;
-    if (d >= d_h) continue;
-#pragma unroll
-    for (int e = 0; e < D_STEP; ++e) dst[d + e] = acc[r * D_STEP + e];
   }
 }
 
@@ -147,13 +191,21 @@ hipError_t launch_combine(float* out, const int32_t* context_lens, const void* w
                           hipStream_t stream) {
   const dim3 grid(H_Q, B), block(64);
   const char* w = static_cast<const char*>(ws);
-  if (d_h % 128 == 0) {
-    hipLaunchKernelGGL((combine_kernel<2>), grid, block, 0, stream, out, context_lens, w, H_Q,
-                       H_KV, d_h, partition_tokens, max_parts);
+#define PKV_COMBINE(VW, R)                                                                    \
+  hipLaunchKernelGGL((combine_kernel<VW, R>), grid, block, 0, stream, out, context_lens, w, H_Q, \
+                     H_KV, d_h, partition_tokens, max_parts)
+  if (d_h % 4 == 0) {
+    PKV_COMBINE(4, 1);  // d_h <= 256: at most 64 columns of 4
+  } else if (d_h <= 64) {
+    PKV_COMBINE(1, 1);
+  } else if (d_h <= 128) {
+    PKV_COMBINE(1, 2);
+  } else if (d_h <= 192) {
+    PKV_COMBINE(1, 3);
   } else {
-    hipLaunchKernelGGL((combine_kernel<1>), grid, block, 0, stream, out, context_lens, w, H_Q,
-                       H_KV, d_h, partition_tokens, max_parts);
+    PKV_COMBINE(1, 4);
   }
+#undef PKV_COMBINE
   return hipGetLastError();
 }
 

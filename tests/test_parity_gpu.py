@@ -109,6 +109,42 @@ def test_kv_append_bit_exact(name, kw):
     assert np.array_equal(as_numpy(vc), rv)
 
 
+def _append_only(w, offset=0):
+    """kv_append alone; offset > 0 shifts every buffer by that many elements
+    off its 16-byte alignment (the kernel then takes its one-element path)."""
+    def place(t):
+        t = t.contiguous()
+        flat = torch.empty(t.numel() + offset, dtype=t.dtype, device=DEV)
+        v = flat[offset:].view(t.shape)
+        v.copy_(t.to(DEV))
+        return v
+    kn, vn, kc, vc = (place(x) for x in (w.k_new[0], w.v_new[0], w.k_cache[0], w.v_cache[0]))
+    ks = w.k_scale[0].to(DEV) if w.k_scale else None
+    vs = w.v_scale[0].to(DEV) if w.v_scale else None
+    pkv.kv_append(kn, vn, kc, vc, w.block_table.to(DEV), w.context_lens.to(DEV), ks, vs)
+    torch.cuda.synchronize()
+    d = _np(w)
+    rk, rv = paged.append(d["k_cache"], d["v_cache"], w.kv_dtype, d["k_new"], d["v_new"],
+                          w.q_dtype, d["table"], d["lens"], w.block_size, d.get("k_scale"),
+                          d.get("v_scale"))
+    assert np.array_equal(as_numpy(kc.cpu()), rk)
+    assert np.array_equal(as_numpy(vc.cpu()), rv)
+
+
+@pytest.mark.parametrize("name,kw,offset", [
+    ("tiny", dict(d_h=6), 0),                                           # d_h % 4 != 0
+    ("llama8b", dict(lens_after=[1, 17, 40], H_Q=4, H_KV=2, d_h=12), 0),  # d_h % 8 != 0
+    ("fp8_gqa", dict(lens_after=[1, 17, 40], H_Q=4, H_KV=2, d_h=20), 0),
+    ("fp8_gqa", dict(lens_after=[1, 17, 40, 300], q_dtype="f32"), 0),   # fp32 -> fp8
+    ("tiny", {}, 1), ("llama8b", dict(lens_after=[1, 17, 40], H_Q=8), 1),
+    ("fp8_gqa", dict(lens_after=[1, 17, 40]), 3),
+], ids=lambda x: str(x)[:30])
+def test_kv_append_vector_and_element_paths(name, kw, offset):
+    w = make_workload(name, **kw)
+    _log(f"append-only {name} {kw} offset={offset}")
+    _append_only(w, offset)
+
+
 def test_fp8_append_exhaustive_bf16_inputs():
     # every bf16 bit pattern (NaN and inf included) x 4 scales through the
     # append kernel; codes must equal the oracle's RNE + saturation encoder
