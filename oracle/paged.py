@@ -1,4 +1,5 @@
-"""Paged decode step: slot mapping, append, gather, exact attention (float64).
+"""Paged attention for decode steps and chunks of new tokens: slot mapping,
+append, gather, exact attention (float64).
 
 Sources on the pages (page 1 = "KV cache: Generation state, latency, and
 allocation"; page 3 = "xf_kv_cache"):
@@ -22,6 +23,16 @@ allocation"; page 3 = "xf_kv_cache"):
   values.  With scale c: s_t = c * q . k_t, w_t = exp(s_t - max s),
   out = sum_t w_t v_t / sum_t w_t.  Subtracting the maximum changes nothing
   mathematically and keeps exp() in range.
+* Chunks of new tokens -- page 1, section 21.3 (chunked prefill): a prompt
+  may be processed in portions; later portions keep the positions and the
+  cached state of the earlier ones.  A chunk of n new tokens of a request
+  whose cache holds ctx positions after the chunk's append occupies
+  positions ctx - n .. ctx - 1, and its query i, at position
+  p = ctx - n + i, reads every position up to and including p (section
+  21.1: a query reads the cached keys of earlier positions and its own).
+  Page 3, "End-to-end flow": the new tokens of a prefix hit attend to the
+  shared prefix through the same block table.  A decode step is the chunk
+  of one token.
 
 Storage formats (``kv_dtype``): "f32" (float32 arrays), "bf16" (uint16 bit
 patterns), "fp8_e4m3" (uint8 codes with one float32 scale per (physical
@@ -83,6 +94,47 @@ def append(k_cache, v_cache, kv_dtype: str, k_new, v_new, in_dtype: str,
                     dst[p, h, r, :] = codecs.e4m3_quantize(xf, np.float32(sc[p, h]))
                 else:
                     raise ValueError(f"unsupported append {in_dtype} -> {kv_dtype}")
+    return kc, vc
+
+
+def _chunk_bounds(query_start, B):
+    qs = [int(x) for x in query_start]
+    if len(qs) != B + 1 or qs[0] != 0 or any(qs[b + 1] < qs[b] for b in range(B)):
+        raise ValueError("query_start must be a non-decreasing prefix sum starting at 0")
+    return qs
+
+
+def append_chunk(k_cache, v_cache, kv_dtype: str, k_new, v_new, in_dtype: str,
+                 block_table, context_lens, query_start, block_size: int,
+                 k_scale=None, v_scale=None, inplace=False):
+    """Write each request's chunk of new K, V rows: row query_start[b] + i of
+    k_new / v_new ([total, H_KV, d_h]) goes to position ctx_b - n_b + i,
+    n_b = query_start[b + 1] - query_start[b].  Stored form as in
+    ``append``; every other pool byte is left untouched."""
+    kc = k_cache if inplace else np.array(k_cache, copy=True)
+    vc = v_cache if inplace else np.array(v_cache, copy=True)
+    num_blocks = kc.shape[0]
+    B = len(context_lens)
+    qs = _chunk_bounds(query_start, B)
+    H_KV = np.shape(k_new)[1]
+    for b in range(B):
+        n_new, ctx = qs[b + 1] - qs[b], int(context_lens[b])
+        if n_new > ctx:
+            raise ValueError("a chunk cannot be longer than the context after it")
+        for i in range(n_new):
+            p, r = slot_of(block_table[b], ctx - n_new + i, block_size)
+            if not 0 <= p < num_blocks:
+                raise ValueError(f"block id {p} outside the pool")
+            for h in range(H_KV):
+                for src, dst, sc in ((k_new, kc, k_scale), (v_new, vc, v_scale)):
+                    x = np.asarray(src[qs[b] + i, h])
+                    if kv_dtype == in_dtype:
+                        dst[p, h, r, :] = x
+                    elif kv_dtype == FP8:
+                        xf = _in_to_f64(x, in_dtype).astype(np.float32)  # exact
+                        dst[p, h, r, :] = codecs.e4m3_quantize(xf, np.float32(sc[p, h]))
+                    else:
+                        raise ValueError(f"unsupported append {in_dtype} -> {kv_dtype}")
     return kc, vc
 
 
@@ -158,6 +210,53 @@ def attend(q, q_dtype: str, k_cache, v_cache, kv_dtype: str, block_table,
             out[b, h * g:(h + 1) * g] = attend_one(qf[b, h * g:(h + 1) * g], K, V,
                                                     softmax_scale)
     return out
+
+
+def attend_chunk(q, q_dtype: str, k_cache, v_cache, kv_dtype: str, block_table,
+                 context_lens, query_start, block_size: int, softmax_scale: float,
+                 k_scale=None, v_scale=None, requests=None) -> np.ndarray:
+    """float64 output [total, H_Q, d_h] of every new query of every chunk:
+    query row query_start[b] + i (position p = ctx_b - n_b + i) attends to
+    positions 0..p of request b.  ``requests`` restricts the computation to
+    some requests (the other rows are NaN)."""
+    qf = _in_to_f64(q, q_dtype)
+    total, H_Q, d_h = qf.shape
+    H_KV = k_cache.shape[1]
+    if H_Q % H_KV:
+        raise ValueError("H_Q must be divisible by H_KV")
+    g = H_Q // H_KV
+    B = len(context_lens)
+    qs = _chunk_bounds(query_start, B)
+    if qs[B] != total:
+        raise ValueError("query_start[B] must equal the number of query rows")
+    out = np.full((total, H_Q, d_h), np.nan, dtype=np.float64)
+    for b in (range(B) if requests is None else requests):
+        n_new, ctx = qs[b + 1] - qs[b], int(context_lens[b])
+        if n_new == 0:
+            continue
+        if n_new > ctx:
+            raise ValueError("a chunk cannot be longer than the context after it")
+        for h in range(H_KV):
+            K = gather_head(k_cache, kv_dtype, k_scale, block_table[b], ctx, h, block_size)
+            V = gather_head(v_cache, kv_dtype, v_scale, block_table[b], ctx, h, block_size)
+            for i in range(n_new):
+                p = ctx - n_new + i
+                out[qs[b] + i, h * g:(h + 1) * g] = attend_one(
+                    qf[qs[b] + i, h * g:(h + 1) * g], K[:p + 1], V[:p + 1], softmax_scale)
+    return out
+
+
+def chunk_step(q, q_dtype, k_new, v_new, k_cache, v_cache, kv_dtype, block_table,
+               context_lens, query_start, block_size, softmax_scale, k_scale=None,
+               v_scale=None, requests=None, inplace=False):
+    """Append every request's chunk, then attend with every new query.
+
+    Returns (k_cache_after, v_cache_after, out)."""
+    kc, vc = append_chunk(k_cache, v_cache, kv_dtype, k_new, v_new, q_dtype, block_table,
+                          context_lens, query_start, block_size, k_scale, v_scale, inplace)
+    out = attend_chunk(q, q_dtype, kc, vc, kv_dtype, block_table, context_lens, query_start,
+                       block_size, softmax_scale, k_scale, v_scale, requests)
+    return kc, vc, out
 
 
 def decode_step(q, q_dtype, k_new, v_new, k_cache, v_cache, kv_dtype,

@@ -1,4 +1,4 @@
-"""Seeded synthetic decode-step inputs.
+"""Seeded synthetic decode-step and chunk inputs.
 
 This module only draws inputs; it holds none of the method's arithmetic (no
 slot mapping, append, gather, softmax or fp8 rounding of its own).  Both the
@@ -19,7 +19,21 @@ measured on:
   each with its own pools and inputs, one shared block table;
 * ``fp8_mqa`` / ``fp8_gqa`` / ``fp8_mha`` -- B=128, H_Q=32, H_KV=1 / 8 / 32,
   fp8 E4M3 K/V with one fp32 scale per (physical block, KV head), bf16 Q,
-  contexts clip(round(2048 * e^Z), 128, 16384) with Z ~ N(0, 1).
+  contexts clip(round(2048 * e^Z), 128, 16384) with Z ~ N(0, 1);
+* ``tiny_chunks`` -- the ``tiny`` shapes with a chunk of new tokens: request
+  0 processes tokens 4..7 of a 12-token prompt taken in chunks of four
+  (page 1, section 21.3), requests 1 and 2 decode one token each (contexts
+  18 and 34 after the step);
+* ``prefix_hit`` -- B=64 requests whose tables map the same 75 blocks (a
+  1,200-token prefix) and then process their 600 unshared prompt tokens as
+  one chunk (page 3, "End-to-end flow"): 38,400 new tokens, each attending
+  to the shared prefix and to the chunk up to itself; Llama-3.1-8B-style
+  heads, bf16, one layer.
+
+Request b brings n_b new tokens (one for a decode step); ``query_start`` is
+their prefix sum ([B + 1], starting at 0), and new K, V and Q rows are laid
+out [sum n_b, heads, d_h] in request order.  For decode workloads this is
+[B, heads, d_h], so their draws are the same as with one token per request.
 
 Recipe (fixed order of draws from one seeded ``torch.Generator``):
 context lengths -> physical-id permutation -> K pool -> V pool -> new K ->
@@ -71,6 +85,12 @@ CONFIGS = {
     "fp8_mha": dict(B=128, H_Q=32, H_KV=32, d_h=128, block_size=16, kv_dtype="fp8_e4m3",
                     q_dtype="bf16", layers=1, seed=4, lens="lognormal", median=2048,
                     lo=128, hi=16384),
+    "tiny_chunks": dict(B=3, H_Q=4, H_KV=2, d_h=8, block_size=4, kv_dtype="f32",
+                        q_dtype="f32", layers=1, seed=5, lens="fixed_after",
+                        lens_after_cfg=(8, 18, 34), new_tokens=(4, 1, 1), pool_blocks=32),
+    "prefix_hit": dict(B=64, H_Q=32, H_KV=8, d_h=128, block_size=16, kv_dtype="bf16",
+                       q_dtype="bf16", layers=1, seed=6, lens="prefix_chunk",
+                       shared_tokens=1200, private_tokens=600),
 }
 
 
@@ -92,12 +112,15 @@ class Workload:
     free_order: torch.Tensor           # int32 [num_blocks - used], ids not in any table
     shared_blocks: int                 # leading table entries shared by every request
     max_context_len: int               # max of context_lens (host value, for grid sizing)
+    query_start: torch.Tensor = None   # int32 [B + 1], prefix sum of new tokens per request
+    total_q: int = 0                   # new tokens in all (rows of q, k_new, v_new)
+    max_q_len: int = 0                 # most new tokens of one request (host value)
     k_cache: list = field(default_factory=list)   # per layer [num_blocks, H_KV, bs, d_h]
     v_cache: list = field(default_factory=list)
     k_scale: list = field(default_factory=list)   # per layer fp32 [num_blocks, H_KV] (fp8 only)
     v_scale: list = field(default_factory=list)
-    q: list = field(default_factory=list)         # per layer [B, H_Q, d_h]
-    k_new: list = field(default_factory=list)     # per layer [B, H_KV, d_h]
+    q: list = field(default_factory=list)         # per layer [total_q, H_Q, d_h]
+    k_new: list = field(default_factory=list)     # per layer [total_q, H_KV, d_h]
     v_new: list = field(default_factory=list)
 
     @property
@@ -110,6 +133,10 @@ def _draw_lens(cfg, B, gen):
     if kind == "fixed":
         before = torch.tensor(cfg["lens_before"][:B], dtype=torch.int64)
         return before + 1
+    if kind == "fixed_after":
+        return torch.tensor(cfg["lens_after_cfg"][:B], dtype=torch.int64)
+    if kind == "prefix_chunk":
+        return torch.full((B,), cfg["shared_tokens"] + cfg["private_tokens"], dtype=torch.int64)
     if kind == "uniform":
         before = torch.randint(cfg["lo"], cfg["hi"] + 1, (B,), generator=gen)
         return before + 1
@@ -133,10 +160,12 @@ def make_workload(name: str, device="cpu", seed=None, **overrides) -> Workload:
     """Draw one decode step of the named workload on ``device``.
 
     ``overrides`` may change B, layers, H_KV, context lengths (``lens_after``
-    as a list) and the pool factor (``pool_factor``) to make small variants
-    for tests; everything else keeps the named workload's recipe."""
+    as a list), new tokens per request (``new_tokens``, a list) and the pool
+    factor (``pool_factor``) to make small variants for tests; everything
+    else keeps the named workload's recipe."""
     cfg = dict(CONFIGS[name])
     lens_after = overrides.pop("lens_after", None)
+    new_tokens = overrides.pop("new_tokens", None)
     pool_factor = overrides.pop("pool_factor", 1.25)
     cfg.update(overrides)
     B, H_Q, H_KV, d_h, bs = cfg["B"], cfg["H_Q"], cfg["H_KV"], cfg["d_h"], cfg["block_size"]
@@ -150,8 +179,20 @@ def make_workload(name: str, device="cpu", seed=None, **overrides) -> Workload:
         B = cfg["B"] = len(lens)
     else:
         lens = _draw_lens(cfg, B, gen)
+    if new_tokens is None:
+        new_tokens = cfg.get("new_tokens", 1)
+        if cfg["lens"] == "prefix_chunk":
+            new_tokens = cfg["private_tokens"]
+    if isinstance(new_tokens, int):
+        new_tokens = [new_tokens] * B
+    new_tokens = [int(x) for x in new_tokens][:B]
+    if len(new_tokens) != B or any(x < 0 or x > int(n) for x, n in zip(new_tokens, lens)):
+        raise ValueError("need 0 <= new tokens <= context length for every request")
+    qstart = torch.tensor([0] + new_tokens, dtype=torch.int64).cumsum(0)
+    total_q = int(qstart[-1])
     nblk = [_ceil_div(int(n), bs) for n in lens]
-    shared = cfg.get("shared_tokens", 0) // bs if cfg["lens"] == "shared" else 0
+    shared = (cfg.get("shared_tokens", 0) // bs
+              if cfg["lens"] in ("shared", "prefix_chunk") else 0)
     needed = shared + sum(nb - shared for nb in nblk)
     num_blocks = cfg.get("pool_blocks") or max(_ceil_div(needed * int(pool_factor * 100), 100), needed)
     num_blocks = max(num_blocks, needed)
@@ -173,7 +214,9 @@ def make_workload(name: str, device="cpu", seed=None, **overrides) -> Workload:
                  num_blocks=num_blocks, max_blocks_per_seq=max_blocks,
                  block_table=table.to(device), context_lens=lens.to(torch.int32).to(device),
                  free_order=free_order, shared_blocks=shared,
-                 max_context_len=int(lens.max().item()))
+                 max_context_len=int(lens.max().item()),
+                 query_start=qstart.to(torch.int32).to(device), total_q=total_q,
+                 max_q_len=max(new_tokens))
 
     # 3.. values, per layer, on the target device
     dgen = torch.Generator(device=device)
@@ -183,9 +226,9 @@ def make_workload(name: str, device="cpu", seed=None, **overrides) -> Workload:
     for _ in range(layers):
         kf = torch.randn(pool_shape, generator=dgen, device=device, dtype=torch.float32)
         vf = torch.randn(pool_shape, generator=dgen, device=device, dtype=torch.float32)
-        kn = torch.randn((B, H_KV, d_h), generator=dgen, device=device).to(qt)
-        vn = torch.randn((B, H_KV, d_h), generator=dgen, device=device).to(qt)
-        q = torch.randn((B, H_Q, d_h), generator=dgen, device=device).to(qt)
+        kn = torch.randn((total_q, H_KV, d_h), generator=dgen, device=device).to(qt)
+        vn = torch.randn((total_q, H_KV, d_h), generator=dgen, device=device).to(qt)
+        q = torch.randn((total_q, H_Q, d_h), generator=dgen, device=device).to(qt)
         if cfg["kv_dtype"] == "fp8_e4m3":
             ks = _fp8_scale(kf, kn)
             vs = _fp8_scale(vf, vn)
