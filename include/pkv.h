@@ -314,12 +314,57 @@ int pkv_combine_partitions(float* out, const int32_t* context_lens, int32_t max_
                            int32_t block_size, int32_t partition_tokens, const void* workspace,
                            size_t workspace_bytes, pkv_stream_t stream);
 
+/* ------------------------------------------------------------------------
+ * Chunks of new tokens (page 1 section 21.3: a prompt processed in chunks
+ * keeps the earlier chunks' positions and cached state; section 21.1: a
+ * query reads the keys of earlier positions and its own; page 3 "xf_kv_cache",
+ * "End-to-end flow": the new tokens after a prefix hit attend to the shared
+ * prefix through the same table).
+ *
+ * Request b brings n_b = query_start[b + 1] - query_start[b] new tokens
+ * (query_start: device int32 [B + 1], non-decreasing, query_start[0] = 0,
+ * query_start[B] = total).  context_lens[b] counts positions after the
+ * chunk's append, so the chunk occupies positions context_lens[b] - n_b ..
+ * context_lens[b] - 1 and needs n_b <= context_lens[b].  Rows of k_new,
+ * v_new ([total][H_KV][d_h]), q and out ([total][H_Q][d_h]) follow request
+ * order.  A decode step is the case n_b = 1 for every request.  Device-side
+ * entries out of range (n_b > context length, rows past `total`) make the
+ * request write nothing.
+ * ---------------------------------------------------------------------- */
+
+/* Write every request's chunk of new K and V rows into their slots (same
+ * stored forms as pkv_kv_append): row query_start[b] + i goes to position
+ * context_lens[b] - n_b + i.  total_tokens = query_start[B] (host value). */
+int pkv_kv_append_chunk(const void* k_new, const void* v_new, int in_dtype, void* k_cache,
+                        void* v_cache, int kv_dtype, const float* k_scale, const float* v_scale,
+                        const int32_t* block_table, int32_t max_blocks_per_seq,
+                        const int32_t* context_lens, const int32_t* query_start, int32_t B,
+                        int32_t total_tokens, int32_t H_KV, int32_t d_h, int32_t block_size,
+                        int32_t num_blocks, pkv_stream_t stream);
+/* Causal attention of every new token: query row query_start[b] + i, at
+ * position p = context_lens[b] - n_b + i, query head hq, KV head hq / g:
+ *   out[row][hq][:] = sum_{t <= p} exp(s_t - max s) V_t / sum_{t <= p} exp(s_t - max s),
+ *   s_t = softmax_scale * q[row][hq] . K_t,
+ * in fp32.  max_q_len (host) >= every n_b sizes the grid; max_context_len
+ * (host) >= every context length.  Same dtype pairs and alignment as
+ * pkv_paged_decode_attention; B and H_Q at most 65535.  No workspace: the
+ * outputs are written directly.  Call after pkv_kv_append_chunk. */
+int pkv_paged_chunk_attention(float* out, const void* q, int q_dtype, const void* k_cache,
+                              const void* v_cache, int kv_dtype, const float* k_scale,
+                              const float* v_scale, const int32_t* block_table,
+                              int32_t max_blocks_per_seq, const int32_t* context_lens,
+                              const int32_t* query_start, int32_t B, int32_t total_q,
+                              int32_t max_q_len, int32_t max_context_len, int32_t H_Q,
+                              int32_t H_KV, int32_t d_h, int32_t block_size, int32_t num_blocks,
+                              float softmax_scale, pkv_stream_t stream);
+
 /* Kernel selection for the attention calls (process-wide, not
  * thread-safe).  AUTO uses the MFMA kernel with the balanced per-wave split
  * where it applies and the generic VALU kernel otherwise; GENERIC, MFMA
  * (balanced split) and MFMA_PARTITION (fixed partitions) force one, and
  * return UNSUPPORTED from the plan and attention calls outside their
- * shapes.  Returns the previous value. */
+ * shapes.  Chunk attention uses its MFMA kernel unless GENERIC is set (or
+ * the shape needs the generic one).  Returns the previous value. */
 typedef enum {
   PKV_VARIANT_AUTO = 0,
   PKV_VARIANT_GENERIC = 1,

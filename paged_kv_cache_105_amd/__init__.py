@@ -17,7 +17,8 @@ from ._lib import (PKV_BF16, PKV_F32, PKV_FP8_E4M3, PKV_VARIANT_AUTO, PKV_VARIAN
 
 __all__ = ["kv_append", "copy_blocks", "decode_plan", "paged_decode_attention", "decode_partitions",
            "combine_partitions", "set_decode_variant", "BlockPool", "PkvError", "load",
-           "prefix_root", "block_hashes", "DIGEST_BYTES",
+           "prefix_root", "block_hashes", "DIGEST_BYTES", "kv_append_chunk",
+           "paged_chunk_attention",
            "PKV_F32", "PKV_BF16", "PKV_FP8_E4M3", "PKV_VARIANT_AUTO", "PKV_VARIANT_GENERIC",
            "PKV_VARIANT_MFMA", "PKV_VARIANT_MFMA_PARTITION", "dtype_code"]
 
@@ -95,6 +96,38 @@ def kv_append(k_new, v_new, k_cache, v_cache, block_table, context_lens,
                                _ptr(v_scale), _ptr(block_table), block_table.shape[1],
                                _ptr(context_lens), B, H_KV, d_h, bs, num_blocks,
                                _stream(stream)), "pkv_kv_append")
+
+
+def kv_append_chunk(k_new, v_new, k_cache, v_cache, block_table, context_lens, query_start,
+                    k_scale=None, v_scale=None, stream=None):
+    """pkv_kv_append_chunk: rows of k_new/v_new [total, H_KV, d_h] go to the
+    last n_b positions of request b (n_b from query_start [B + 1])."""
+    total, H_KV, d_h = k_new.shape
+    num_blocks, _, bs, _ = k_cache.shape
+    B = context_lens.shape[0]
+    check(load().pkv_kv_append_chunk(_ptr(k_new), _ptr(v_new), _dtype_code(k_new),
+                                     _ptr(k_cache), _ptr(v_cache), _dtype_code(k_cache),
+                                     _ptr(k_scale), _ptr(v_scale), _ptr(block_table),
+                                     block_table.shape[1], _ptr(context_lens),
+                                     _ptr(query_start), B, total, H_KV, d_h, bs, num_blocks,
+                                     _stream(stream)), "pkv_kv_append_chunk")
+
+
+def paged_chunk_attention(out, q, k_cache, v_cache, block_table, context_lens, query_start,
+                          max_q_len, max_context_len, softmax_scale, k_scale=None,
+                          v_scale=None, stream=None):
+    """pkv_paged_chunk_attention: out [total, H_Q, d_h] float32."""
+    total, H_Q, d_h = q.shape
+    num_blocks, H_KV, bs, _ = k_cache.shape
+    B = context_lens.shape[0]
+    check(load().pkv_paged_chunk_attention(_ptr(out), _ptr(q), _dtype_code(q), _ptr(k_cache),
+                                           _ptr(v_cache), _dtype_code(k_cache), _ptr(k_scale),
+                                           _ptr(v_scale), _ptr(block_table),
+                                           block_table.shape[1], _ptr(context_lens),
+                                           _ptr(query_start), B, total, max_q_len,
+                                           max_context_len, H_Q, H_KV, d_h, bs, num_blocks,
+                                           softmax_scale, _stream(stream)),
+          "pkv_paged_chunk_attention")
 
 
 def copy_blocks(k_cache, v_cache, pairs, k_scale=None, v_scale=None, stream=None):

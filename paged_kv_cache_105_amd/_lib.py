@@ -65,6 +65,11 @@ SIGNATURES = {
                                         _i32, _vp, _sz, _vp]),
     "pkv_combine_partitions": (C.c_int, [_vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
                                          _vp, _sz, _vp]),
+    "pkv_kv_append_chunk": (C.c_int, [_vp, _vp, C.c_int, _vp, _vp, C.c_int, _vp, _vp, _vp, _i32,
+                                      _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp]),
+    "pkv_paged_chunk_attention": (C.c_int, [_vp, _vp, C.c_int, _vp, _vp, C.c_int, _vp, _vp, _vp,
+                                            _i32, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
+                                            _i32, _i32, _i32, _f, _vp]),
     "pkv_set_decode_variant": (C.c_int, [C.c_int]),
 }
 

@@ -19,8 +19,14 @@ namespace pkv {
 hipError_t launch_kv_append(int in_dtype, int kv_dtype, const void* k_new, const void* v_new,
                             void* k_cache, void* v_cache, const float* k_scale,
                             const float* v_scale, const int32_t* block_table,
-                            int max_blocks_per_seq, const int32_t* context_lens, int B, int H_KV,
-                            int d_h, int block_size, int num_blocks, hipStream_t stream);
+                            int max_blocks_per_seq, const int32_t* context_lens,
+                            const int32_t* query_start, int B, int rows, int H_KV, int d_h,
+                            int block_size, int num_blocks, hipStream_t stream);
+bool chunk_mfma_supports(int q_dtype, int kv_dtype, int d_h, int block_size);
+hipError_t launch_chunk_mfma(int kv_dtype, int max_q_len, const DecodeArgs& a,
+                             hipStream_t stream);
+hipError_t launch_chunk_generic(int q_dtype, int kv_dtype, const DecodeArgs& a,
+                                hipStream_t stream);
 hipError_t launch_decode_generic(int q_dtype, int kv_dtype, const DecodeArgs& a,
                                  hipStream_t stream);
 size_t generic_lds_bytes(int g, int d_h, int partition_tokens);
@@ -223,11 +229,15 @@ int pkv_set_decode_variant(int variant) {
   return prev;
 }
 
-int pkv_kv_append(const void* k_new, const void* v_new, int in_dtype, void* k_cache,
-                  void* v_cache, int kv_dtype, const float* k_scale, const float* v_scale,
-                  const int32_t* block_table, int32_t max_blocks_per_seq,
-                  const int32_t* context_lens, int32_t B, int32_t H_KV, int32_t d_h,
-                  int32_t block_size, int32_t num_blocks, pkv_stream_t stream) {
+}  // extern "C"
+
+namespace {
+
+int check_append_args(const void* k_new, const void* v_new, int in_dtype, void* k_cache,
+                      void* v_cache, int kv_dtype, const float* k_scale, const float* v_scale,
+                      const int32_t* block_table, int32_t max_blocks_per_seq,
+                      const int32_t* context_lens, int32_t B, int32_t H_KV, int32_t d_h,
+                      int32_t block_size, int32_t num_blocks) {
   if (!k_new || !v_new || !k_cache || !v_cache || !block_table || !context_lens)
     return PKV_ERR_INVALID_ARG;
   if (!valid_dtype(in_dtype) || !valid_dtype(kv_dtype) || in_dtype == PKV_FP8_E4M3)
@@ -238,10 +248,89 @@ int pkv_kv_append(const void* k_new, const void* v_new, int in_dtype, void* k_ca
   if (kv_dtype == PKV_FP8_E4M3 && (!k_scale || !v_scale)) return PKV_ERR_INVALID_ARG;
   const bool pair_ok = (in_dtype == kv_dtype) || kv_dtype == PKV_FP8_E4M3;
   if (!pair_ok) return PKV_ERR_UNSUPPORTED;
+  return PKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int pkv_kv_append(const void* k_new, const void* v_new, int in_dtype, void* k_cache,
+                  void* v_cache, int kv_dtype, const float* k_scale, const float* v_scale,
+                  const int32_t* block_table, int32_t max_blocks_per_seq,
+                  const int32_t* context_lens, int32_t B, int32_t H_KV, int32_t d_h,
+                  int32_t block_size, int32_t num_blocks, pkv_stream_t stream) {
+  const int st = check_append_args(k_new, v_new, in_dtype, k_cache, v_cache, kv_dtype, k_scale,
+                                   v_scale, block_table, max_blocks_per_seq, context_lens, B,
+                                   H_KV, d_h, block_size, num_blocks);
+  if (st != PKV_OK) return st;
   return hip_status(pkv::launch_kv_append(in_dtype, kv_dtype, k_new, v_new, k_cache, v_cache,
                                           k_scale, v_scale, block_table, max_blocks_per_seq,
-                                          context_lens, B, H_KV, d_h, block_size, num_blocks,
+                                          context_lens, nullptr, B, B, H_KV, d_h, block_size,
+                                          num_blocks, static_cast<hipStream_t>(stream)));
+}
+
+int pkv_kv_append_chunk(const void* k_new, const void* v_new, int in_dtype, void* k_cache,
+                        void* v_cache, int kv_dtype, const float* k_scale, const float* v_scale,
+                        const int32_t* block_table, int32_t max_blocks_per_seq,
+                        const int32_t* context_lens, const int32_t* query_start, int32_t B,
+                        int32_t total_tokens, int32_t H_KV, int32_t d_h, int32_t block_size,
+                        int32_t num_blocks, pkv_stream_t stream) {
+  const int st = check_append_args(k_new, v_new, in_dtype, k_cache, v_cache, kv_dtype, k_scale,
+                                   v_scale, block_table, max_blocks_per_seq, context_lens, B,
+                                   H_KV, d_h, block_size, num_blocks);
+  if (st != PKV_OK) return st;
+  if (!query_start || total_tokens < 0) return PKV_ERR_INVALID_ARG;
+  if (total_tokens == 0) return PKV_OK;
+  return hip_status(pkv::launch_kv_append(in_dtype, kv_dtype, k_new, v_new, k_cache, v_cache,
+                                          k_scale, v_scale, block_table, max_blocks_per_seq,
+                                          context_lens, query_start, B, total_tokens, H_KV, d_h,
+                                          block_size, num_blocks,
                                           static_cast<hipStream_t>(stream)));
+}
+
+int pkv_paged_chunk_attention(float* out, const void* q, int q_dtype, const void* k_cache,
+                              const void* v_cache, int kv_dtype, const float* k_scale,
+                              const float* v_scale, const int32_t* block_table,
+                              int32_t max_blocks_per_seq, const int32_t* context_lens,
+                              const int32_t* query_start, int32_t B, int32_t total_q,
+                              int32_t max_q_len, int32_t max_context_len, int32_t H_Q,
+                              int32_t H_KV, int32_t d_h, int32_t block_size, int32_t num_blocks,
+                              float softmax_scale, pkv_stream_t stream) {
+  int st = check_attention_args(out, q, q_dtype, k_cache, v_cache, kv_dtype, k_scale, v_scale,
+                                block_table, max_blocks_per_seq, context_lens, max_context_len,
+                                B, H_Q, H_KV, d_h, block_size, num_blocks, softmax_scale);
+  if (st != PKV_OK) return st;
+  if (!query_start || total_q < 0 || max_q_len < 1 || max_q_len > max_context_len ||
+      B > 65535 || H_Q > 65535)
+    return PKV_ERR_INVALID_ARG;
+  if (total_q == 0) return PKV_OK;
+
+  pkv::DecodeArgs a{};
+  a.out = out;
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
+  a.block_table = block_table;
+  a.context_lens = context_lens;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.B = B;
+  a.H_Q = H_Q;
+  a.H_KV = H_KV;
+  a.g = H_Q / H_KV;
+  a.d_h = d_h;
+  a.block_size = block_size;
+  a.num_blocks = num_blocks;
+  a.scale_log2 = softmax_scale * pkv::kLog2e;
+  a.query_start = query_start;
+  a.total_q = total_q;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool mfma = g_variant != PKV_VARIANT_GENERIC &&
+                    pkv::chunk_mfma_supports(q_dtype, kv_dtype, d_h, block_size);
+  return hip_status(mfma ? pkv::launch_chunk_mfma(kv_dtype, max_q_len, a, s)
+                         : pkv::launch_chunk_generic(q_dtype, kv_dtype, a, s));
 }
 
 int pkv_copy_blocks(void* k_cache, void* v_cache, int kv_dtype, float* k_scale, float* v_scale,

@@ -4,9 +4,14 @@
 // section 21.5: position t sits in logical block t / bs, slot t % bs, and the
 // block table gives the physical block).
 //
-// Grid (request, chunk of the request's K and V elements); each thread moves
-// a run of consecutive elements of one head's row with one load and one
-// store.  Bit copies for equal dtypes, OCP E4M3 quantisation with the
+// Chunks of new tokens (page 1 section 21.3) use the same kernel: with a
+// query_start array, row r of k_new / v_new belongs to the request b whose
+// range [query_start[b], query_start[b + 1]) holds it and goes to position
+// context_lens[b] - n_b + (r - query_start[b]), n_b the request's new
+// tokens; without one, row b is request b's single new token.
+//
+// Grid (row, chunk of the row's K and V elements); each thread moves a run
+// of consecutive elements of one head's row with one load and one store.  Bit copies for equal dtypes, OCP E4M3 quantisation with the
 // per-(block, head) scale for fp8 caches.  A request whose slot would fall
 // outside the table or the pool writes nothing.
 
@@ -45,14 +50,26 @@ __global__ __launch_bounds__(256) void kv_append_kernel(
     const void* __restrict__ k_new, const void* __restrict__ v_new, void* __restrict__ k_cache,
     void* __restrict__ v_cache, const float* __restrict__ k_scale,
     const float* __restrict__ v_scale, const int32_t* __restrict__ block_table,
-    int max_blocks_per_seq, const int32_t* __restrict__ context_lens, int H_KV, int d_h,
+    int max_blocks_per_seq, const int32_t* __restrict__ context_lens,
+    const int32_t* __restrict__ query_start, int B, int total_rows, int H_KV, int d_h,
     int block_size, int num_blocks) {
   constexpr int IB = IN == DT_F32 ? 4 : 2;   // input bytes per element
   constexpr int OB = KV == DT_F32 ? 4 : KV == DT_BF16 ? 2 : 1;
-  const int b = blockIdx.x;
-  const int n = context_lens[b];
-  if (n < 1 || n > max_blocks_per_seq * block_size) return;
-  const int t = n - 1;
+  const int row_id = blockIdx.x;
+  int b = row_id, t;
+  if (query_start) {
+    b = request_of_row(query_start, B, row_id);
+    const int qs0 = query_start[b], qs1 = query_start[b + 1];
+    const int n = context_lens[b];
+    if (qs0 < 0 || qs1 > total_rows || row_id < qs0 || row_id >= qs1 || qs1 - qs0 > n ||
+        n > max_blocks_per_seq * block_size)
+      return;
+    t = n - (qs1 - qs0) + (row_id - qs0);
+  } else {
+    const int n = context_lens[b];
+    if (n < 1 || n > max_blocks_per_seq * block_size) return;
+    t = n - 1;
+  }
   const int p = block_table[static_cast<size_t>(b) * max_blocks_per_seq + t / block_size];
   if (p < 0 || p >= num_blocks) return;
   const int r = t % block_size;
@@ -63,7 +80,7 @@ __global__ __launch_bounds__(256) void kv_append_kernel(
   const int e = is_v ? i - row : i;
   const int h = e / d_h, d = e % d_h;
   const char* src = static_cast<const char*>(is_v ? v_new : k_new) +
-                    (static_cast<size_t>(b) * row + e) * IB;
+                    (static_cast<size_t>(row_id) * row + e) * IB;
   char* dst = static_cast<char*>(is_v ? v_cache : k_cache) +
               (((static_cast<size_t>(p) * H_KV + h) * block_size + r) * d_h + d) * OB;
   if constexpr (IN == KV) {
@@ -95,8 +112,9 @@ __global__ __launch_bounds__(256) void kv_append_kernel(
 hipError_t launch_kv_append(int in_dtype, int kv_dtype, const void* k_new, const void* v_new,
                             void* k_cache, void* v_cache, const float* k_scale,
                             const float* v_scale, const int32_t* block_table,
-                            int max_blocks_per_seq, const int32_t* context_lens, int B, int H_KV,
-                            int d_h, int block_size, int num_blocks, hipStream_t stream) {
+                            int max_blocks_per_seq, const int32_t* context_lens,
+                            const int32_t* query_start, int B, int rows, int H_KV, int d_h,
+                            int block_size, int num_blocks, hipStream_t stream) {
   // elements per thread: a 16-byte input access where d_h and the buffers'
   // alignment allow it (4 for fp8 output from fp32), else one element
   const int in_b = in_dtype == DT_F32 ? 4 : 2;
@@ -108,11 +126,11 @@ hipError_t launch_kv_append(int in_dtype, int kv_dtype, const void* k_new, const
   const int ept = vec ? want : 1;
   const int total = 2 * H_KV * d_h / ept;  // threads per request
   const int threads = total >= 256 ? 256 : 64;
-  const dim3 grid(B, (total + threads - 1) / threads), block(threads);
+  const dim3 grid(rows, (total + threads - 1) / threads), block(threads);
 #define PKV_APPEND(IN, KV, EPT)                                                              \
   hipLaunchKernelGGL((kv_append_kernel<IN, KV, EPT>), grid, block, 0, stream, k_new, v_new,  \
                      k_cache, v_cache, k_scale, v_scale, block_table, max_blocks_per_seq,    \
-                     context_lens, H_KV, d_h, block_size, num_blocks)
+                     context_lens, query_start, B, rows, H_KV, d_h, block_size, num_blocks)
 #define PKV_APPEND_EPT(IN, KV, W) \
   do {                            \
     if (vec) PKV_APPEND(IN, KV, W); \

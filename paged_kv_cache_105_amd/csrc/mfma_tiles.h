@@ -1,0 +1,337 @@
+// MFMA tiles of paged attention on gfx950 (d_h = 128, 16-slot blocks, bf16
+// or fp8 E4M3 caches, bf16 queries): the per-block step shared by the decode
+// kernels and the chunk kernel.
+//
+// Page 1 "KV cache: Generation state, latency, and allocation", section 21.1:
+// the query heads of a group read the same KV head but keep separate scores
+// and normalise them over the positions they see; section 21.5: positions
+// are read through the block table.  A wave holds up to NG x 16 "columns"
+// (a query head of one query position each) and folds every K/V block it
+// loads into all of them:
+//
+//   S[token][column] = K_blk[16 x 128] . Q^T[128 x 16]     (4 x MFMA 16x16x32)
+//   O^T[dim][column] += V_blk^T[128 x 16] . P^T[16 x 16]   (8 x 2 x MFMA 16x16x16)
+//
+// Lane l = 16 q + c (q = l / 16, c = l % 16).  Layouts:
+//   * A coalesced 1 KiB load s (s = 0..3) of a bf16 block gives lane l the
+//     8 dims 8c..8c+7 of token 4s + q.  fp8 blocks use 512 B loads with the
+//     same token/dim assignment (8 codes per lane), widened to bf16.
+//   * QK uses row r of the MFMA A operand for token pi(r) = r/4 + 4(r%4)
+//     and reads K through LDS (16 B per lane, XOR-swizzled by chunk so that
+//     both the row-major writes and the per-row reads are conflict free).
+//     Its result then gives lane l the scores of tokens q + 4i (i = 0..3)
+//     for column c -- exactly the B operand layout of the PV product with
+//     the same token permutation, so P never moves between lanes.
+//   * PV step n (n = 0..7) uses A-operand row c for dim 8c + n and k-index
+//     4q + i for token q + 4i: lane l already holds V[q + 4i][8c + n] from
+//     load s = i, so V needs one byte-permute per pair of values and no LDS.
+//   * The accumulator of step n gives lane l column c, dims 32q + 8i + n:
+//     every lane owns one column's running max and sum, and rescales its own
+//     accumulators.
+// Probabilities enter the bf16 MFMA as a hi + lo pair of bf16 values, so
+// the weights keep ~16 significant bits; the running max moves only when a
+// block exceeds it by more than 2^8, which spares most rescales.  Positions
+// a column must not see get probability 0, and V rows past the cached
+// positions are zeroed before the product, so garbage or NaN in unused
+// slots is never mixed in.
+
+#pragma once
+
+#include "pkv_device.h"
+
+namespace pkv {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kD = 128;
+constexpr int kBS = 16;
+
+// 4 E4M3 codes -> 4 bf16 values (two packed dwords), exact: gfx950 converts
+// a pair of OCP E4M3 codes to bf16 in one instruction (scale 1.0; every E4M3
+// value is a bf16 value).
+__device__ __forceinline__ u32x2 fp8x4_to_bf16x4(uint32_t w) {
+  u32x2 r;
+  r.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false));
+  r.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true));
+  return r;
+}
+
+template <int KV>
+struct Raw;  // one block of K or V as loaded by a lane
+template <>
+struct Raw<DT_BF16> {
+  u32x4 w[4];
+};
+template <>
+struct Raw<DT_FP8> {
+  u32x2 w[4];
+  float scale;  // the block's scale for this KV head, loaded with the block
+};
+
+// A decode step streams the cache: each tile is read once, so the loads
+// carry the non-temporal hint (NT) and do not displace other data from the
+// L2 and last-level caches (measured: +10-12% gather bandwidth on MI355X).
+// Chunk attention reads each tile once per column tile and keeps the hint
+// off, so the other column tiles of the same request find it in L2.
+template <int KV, bool NT>
+__device__ __forceinline__ void load_raw(Raw<KV>& r, const char* base, int lane) {
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    if constexpr (KV == DT_BF16) {
+      const u32x4* src = reinterpret_cast<const u32x4*>(base + s * 1024 + lane * 16);
+      r.w[s] = NT ? __builtin_nontemporal_load(src) : *src;
+    } else {
+      const u32x2* src = reinterpret_cast<const u32x2*>(base + s * 512 + lane * 8);
+      r.w[s] = NT ? __builtin_nontemporal_load(src) : *src;
+    }
+  }
+}
+
+// chunk s as 8 bf16 values (4 dwords: dims 8c+2k, 8c+2k+1 in dword k)
+template <int KV>
+__device__ __forceinline__ u32x4 as_bf16x8(const Raw<KV>& r, int s) {
+  if constexpr (KV == DT_BF16) {
+    return r.w[s];
+  } else {
+    const u32x2 lo = fp8x4_to_bf16x4(r.w[s].x), hi = fp8x4_to_bf16x4(r.w[s].y);
+    u32x4 o;
+    o.x = lo.x;
+    o.y = lo.y;
+    o.z = hi.x;
+    o.w = hi.y;
+    return o;
+  }
+}
+
+// LDS ordering inside one wave: LDS instructions of a wave execute in issue
+// order, so only the compiler must be kept from moving LDS accesses across
+// this point, and the writes must have completed.  No s_barrier and no wait
+// on outstanding global loads (a workgroup fence would add vmcnt(0) and
+// drain the prefetched blocks).
+__device__ __forceinline__ void lds_wave_sync() {
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0); vmcnt and expcnt untouched
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// Running softmax state of one wave for the g heads of its KV head.
+template <int NG>
+struct Acc {
+  f32x4 o[NG][8];
+  float m[NG], l[NG];
+};
+
+// Per-lane constants of the K transpose through LDS.
+struct LaneMap {
+  int lane, q4, c;
+  int wpos[4], rpos[4];
+};
+
+__device__ __forceinline__ LaneMap lane_map() {
+  LaneMap L;
+  L.lane = threadIdx.x;
+  L.q4 = L.lane >> 4;
+  L.c = L.lane & 15;
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const int t = 4 * s + L.q4;                      // token written by this lane
+    const int f = 4 * (t & 3) + (t >> 2);            // pi^-1(t)
+    L.wpos[s] = t * 16 + (L.c ^ f);
+  }
+  const int rtok = (L.c >> 2) + 4 * (L.c & 3);       // pi(c): token read by this lane
+#pragma unroll
+  for (int j = 0; j < 4; ++j) L.rpos[j] = rtok * 16 + ((4 * j + L.q4) ^ L.c);
+  return L;
+}
+
+template <int NG>
+__device__ __forceinline__ void acc_init(Acc<NG>& acc) {
+#pragma unroll
+  for (int G = 0; G < NG; ++G) {
+    acc.m[G] = -INFINITY;
+    acc.l[G] = 0.f;
+#pragma unroll
+    for (int nn = 0; nn < 8; ++nn) acc.o[G][nn] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+}
+
+// Running-max slack (log2 units): the running max m is raised only when a
+// block's max exceeds it by more than this, so most blocks skip the rescale
+// of the accumulators.  Probabilities 2^(s - m) then stay below 2^8, well
+// inside fp32 and the hi + lo bf16 split.  The result is the same softmax:
+// o and l are both relative to whatever m is current.
+constexpr float kRescaleSlack = 8.0f;
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Two floats to two bf16 (round to nearest even), packed in one dword.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
+}
+
+// One block of 16 positions: QK, online softmax, PV.  `valid` counts the
+// block's positions that hold cached entries (<= 0 for a padding step,
+// which leaves the state unchanged); V rows at or past it are zeroed.  A
+// score of this lane's column of group G counts only for tokens
+// <= lim[G] (block-relative); `full` (uniform) says that every column sees
+// all 16 tokens, so no score needs a mask.
+template <int KV, int NG>
+__device__ __forceinline__ void process_block(float scale_log2, const LaneMap& L,
+                                              u32x4* lds_k, const bf16x8 (&qop)[NG][4],
+                                              Acc<NG>& acc, const Raw<KV>& kr,
+                                              const Raw<KV>& vr, int valid, bool full,
+                                              const int (&lim)[NG]) {
+  // ---- K: widen, transpose through LDS, QK on the matrix cores
+#pragma unroll
+  for (int s = 0; s < 4; ++s) lds_k[L.wpos[s]] = as_bf16x8<KV>(kr, s);
+  lds_wave_sync();
+  bf16x8 ka[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) ka[j] = __builtin_bit_cast(bf16x8, lds_k[L.rpos[j]]);
+
+  float kscale = scale_log2;
+  float vscale = 1.0f;
+  if constexpr (KV == DT_FP8) {
+    kscale *= kr.scale;
+    vscale = vr.scale;
+  }
+
+  // ---- V operands: token q + 4i, dim 8c + n  (zero the invalid rows)
+  u32x4 vb[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) vb[s] = as_bf16x8<KV>(vr, s);
+  if (valid < kBS) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+      if (4 * s + L.q4 >= valid) vb[s] = u32x4{0u, 0u, 0u, 0u};
+  }
+
+#pragma unroll
+  for (int G = 0; G < NG; ++G) {
+    f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[j], qop[G][j], sc, 0, 0, 0);
+
+    // online softmax for head 16G + c over tokens q + 4i
+    float s2[4];
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) s2[ii] = sc[ii] * kscale;
+    if (!full) {
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii)
+        if (L.q4 + 4 * ii > lim[G]) s2[ii] = -INFINITY;
+    }
+    float mx = fmaxf(fmaxf(s2[0], s2[1]), fmaxf(s2[2], s2[3]));
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    // raise the running max only when needed (uniform branch over the wave;
+    // the first real block always takes it since m starts at -inf)
+    if (__any(mx > acc.m[G] + kRescaleSlack)) {
+      const float m_new = fmaxf(acc.m[G], mx);
+      const float alpha = __builtin_amdgcn_exp2f(acc.m[G] - m_new);
+      acc.l[G] *= alpha;
+#pragma unroll
+      for (int nn = 0; nn < 8; ++nn) acc.o[G][nn] *= alpha;
+      acc.m[G] = m_new;
+    }
+    float pr[4];
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) pr[ii] = __builtin_amdgcn_exp2f(s2[ii] - acc.m[G]);  // 0 if invalid
+    acc.l[G] += (pr[0] + pr[1]) + (pr[2] + pr[3]);
+
+    // probabilities (times the V scale) as hi + lo bf16 pairs
+    if constexpr (KV == DT_FP8) {
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) pr[ii] *= vscale;
+    }
+    const uint32_t h01 = pack_bf16x2(pr[0], pr[1]), h23 = pack_bf16x2(pr[2], pr[3]);
+    const uint32_t l01 = pack_bf16x2(pr[0] - __uint_as_float(h01 << 16),
+                                     pr[1] - __uint_as_float(h01 & 0xffff0000u));
+    const uint32_t l23 = pack_bf16x2(pr[2] - __uint_as_float(h23 << 16),
+                                     pr[3] - __uint_as_float(h23 & 0xffff0000u));
+    const i16x4 ph = __builtin_bit_cast(i16x4, u32x2{h01, h23});
+    const i16x4 pl = __builtin_bit_cast(i16x4, u32x2{l01, l23});
+
+#pragma unroll
+    for (int nn = 0; nn < 8; ++nn) {
+      const uint32_t sel = (nn & 1) ? 0x07060302u : 0x05040100u;
+      const int k = nn >> 1;
+      u32x2 av;
+      av.x = __builtin_amdgcn_perm(vb[1][k], vb[0][k], sel);
+      av.y = __builtin_amdgcn_perm(vb[3][k], vb[2][k], sel);
+      const i16x4 va = __builtin_bit_cast(i16x4, av);
+      acc.o[G][nn] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, ph, acc.o[G][nn], 0, 0, 0);
+      acc.o[G][nn] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pl, acc.o[G][nn], 0, 0, 0);
+    }
+  }
+  // the K tile in LDS is rewritten by the next block: keep its reads first
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// Blocks [jb, je) of KV head h of one request (table row `row`, cached
+// positions < n) folded into `acc`.  Column (lane c of group G) sees the
+// positions <= pcol[G]; p_first (uniform) is the smallest of them.  Decode
+// passes n - 1 for all.  Table entries are read 64 at a time, one per lane.
+// Within each group of up to 64 blocks, loads run DEPTH blocks ahead of the
+// block being processed.  The step count is padded to a multiple of
+// DEPTH + 1 so that every unrolled step issues and processes
+// unconditionally: a load past the group's last block re-reads that block
+// (an L2 hit), and a padding step sees no valid position.  The number of
+// loads in flight -- and every wait count -- is then the same on every path.
+template <int KV, int NG, int DEPTH, bool NT = true>
+__device__ __forceinline__ void run_blocks(const DecodeArgs& a, const LaneMap& L, u32x4* lds_k,
+                                           const bf16x8 (&qop)[NG][4], Acc<NG>& acc,
+                                           const int32_t* row, int n, int h, int jb, int je,
+                                           int p_first, const int (&pcol)[NG]) {
+  constexpr int kElem = (KV == DT_BF16) ? 2 : 1;
+  const size_t head_bytes = static_cast<size_t>(kBS) * kD * kElem;
+  const size_t blk_bytes = head_bytes * a.H_KV;
+  const char* kbase = static_cast<const char*>(a.k_cache) + h * head_bytes;
+  const char* vbase = static_cast<const char*>(a.v_cache) + h * head_bytes;
+  const int end_pos = min(n, je * kBS);
+
+  for (int g0 = jb; g0 < je; g0 += 64) {
+    const int nblk = min(64, je - g0);
+    int my_blk = 0;
+    if (L.lane < nblk) my_blk = min(max(row[g0 + L.lane], 0), a.num_blocks - 1);
+
+    Raw<KV> kbuf[DEPTH + 1], vbuf[DEPTH + 1];
+    auto issue = [&](Raw<KV>& kr, Raw<KV>& vr, int i) {
+      const int p = __builtin_amdgcn_readlane(my_blk, min(i, nblk - 1));
+      load_raw<KV, NT>(kr, kbase + p * blk_bytes, L.lane);
+      load_raw<KV, NT>(vr, vbase + p * blk_bytes, L.lane);
+      if constexpr (KV == DT_FP8) {
+        kr.scale = a.k_scale[static_cast<size_t>(p) * a.H_KV + h];
+        vr.scale = a.v_scale[static_cast<size_t>(p) * a.H_KV + h];
+      }
+      // keep the scheduler from sinking these loads below the block being
+      // processed (that would shrink the distance they run ahead)
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    const int nsteps = (nblk + DEPTH) / (DEPTH + 1) * (DEPTH + 1);
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d) issue(kbuf[d], vbuf[d], d);
+    for (int i0 = 0; i0 < nsteps; i0 += DEPTH + 1) {
+#pragma unroll
+      for (int u = 0; u <= DEPTH; ++u) {
+        const int i = i0 + u;
+        issue(kbuf[(u + DEPTH) % (DEPTH + 1)], vbuf[(u + DEPTH) % (DEPTH + 1)], i + DEPTH);
+        const int t0 = (g0 + i) * kBS;
+        const int valid = (i < nblk) ? end_pos - t0 : 0;
+        const bool full = valid >= kBS && t0 + kBS - 1 <= p_first;
+        int lim[NG];
+#pragma unroll
+        for (int G = 0; G < NG; ++G) lim[G] = min(pcol[G] - t0, valid - 1);
+        process_block<KV, NG>(a.scale_log2, L, lds_k, qop, acc, kbuf[u], vbuf[u], valid, full,
+                              lim);
+      }
+    }
+  }
+}
+
+}  // namespace pkv

@@ -151,6 +151,22 @@ struct DecodeArgs {
   int32_t B, H_Q, H_KV, g, d_h, block_size, num_blocks;
   int32_t partition_tokens, max_parts;
   float scale_log2;  // softmax_scale * log2(e)
+  // chunk attention only: [B + 1] prefix sum of each request's new tokens
+  // (query rows), nullptr for a decode step (one query row per request), and
+  // the number of query rows
+  const int32_t* query_start;
+  int32_t total_q;
 };
+
+// Request of query row r: the last b with query_start[b] <= r (binary
+// search; query_start is non-decreasing).  Used by the chunk kernels.
+__device__ __forceinline__ int request_of_row(const int32_t* query_start, int B, int r) {
+  int lo = 0, hi = B - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (query_start[mid] <= r) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
 
 }  // namespace pkv

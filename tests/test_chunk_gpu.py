@@ -1,0 +1,254 @@
+"""GPU parity of chunk attention (several new tokens per request) through the
+C ABI against the float64 oracle.
+
+* pkv_kv_append_chunk: every byte of both pools bit-exact against the
+  oracle's chunk append (untouched slots included), f32 / bf16 / fp8;
+* pkv_paged_chunk_attention: max |gpu - oracle| <= 2e-3 on every output, for
+  the MFMA kernel and the generic kernel, every group size 1..32, bf16 and
+  fp8 caches, chunks that start mid-block, span many blocks, cover the whole
+  context, or are empty;
+* page 1 "KV cache: Generation state, latency, and allocation", section
+  21.3: a twelve-token prompt in chunks of four gives the outputs of the
+  whole prompt as one chunk;
+* a chunk of one token per request agrees with the decode kernel;
+* unused slots holding NaN are never read;
+* page 3 "xf_kv_cache", "End-to-end flow", at full size: 64 requests share a
+  75-block prefix and process 600 new tokens each; sampled requests.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import paged_kv_cache_105_amd as pkv
+from oracle import paged
+from paged_kv_cache_105_amd.workloads import as_numpy, make_workload
+
+pytestmark = pytest.mark.gpu
+TOL = 2e-3
+DEV = torch.device("cuda:0")
+KERNELS = [pkv.PKV_VARIANT_AUTO, pkv.PKV_VARIANT_GENERIC]
+KIDS = ["mfma", "generic"]
+
+
+def _log(msg):
+    print(msg, flush=True)
+
+
+def _np(w):
+    d = dict(q=as_numpy(w.q[0]), k_new=as_numpy(w.k_new[0]), v_new=as_numpy(w.v_new[0]),
+             k_cache=as_numpy(w.k_cache[0]).copy(), v_cache=as_numpy(w.v_cache[0]).copy(),
+             table=as_numpy(w.block_table), lens=as_numpy(w.context_lens),
+             qs=as_numpy(w.query_start))
+    if w.kv_dtype == "fp8_e4m3":
+        d["ks"], d["vs"] = as_numpy(w.k_scale[0]), as_numpy(w.v_scale[0])
+    return d
+
+
+def gpu_chunk(w, variant=pkv.PKV_VARIANT_AUTO, kc=None, vc=None, append=True):
+    g = lambda t: t.to(DEV).contiguous()
+    k_cache = g(w.k_cache[0] if kc is None else kc)
+    v_cache = g(w.v_cache[0] if vc is None else vc)
+    bt, cl, qs = g(w.block_table), g(w.context_lens), g(w.query_start)
+    ks = g(w.k_scale[0]) if w.k_scale else None
+    vs = g(w.v_scale[0]) if w.v_scale else None
+    if append:
+        pkv.kv_append_chunk(g(w.k_new[0]), g(w.v_new[0]), k_cache, v_cache, bt, cl, qs, ks, vs)
+    out = torch.full((w.total_q, w.H_Q, w.d_h), float("nan"), dtype=torch.float32, device=DEV)
+    prev = pkv.set_decode_variant(variant)
+    try:
+        pkv.paged_chunk_attention(out, g(w.q[0]), k_cache, v_cache, bt, cl, qs,
+                                  max(w.max_q_len, 1), w.max_context_len, w.softmax_scale,
+                                  ks, vs)
+    finally:
+        pkv.set_decode_variant(prev)
+    torch.cuda.synchronize()
+    return k_cache.cpu(), v_cache.cpu(), out.cpu().numpy().astype(np.float64)
+
+
+def oracle_chunk(w, d, requests=None):
+    return paged.chunk_step(d["q"], w.q_dtype, d["k_new"], d["v_new"], d["k_cache"],
+                            d["v_cache"], w.kv_dtype, d["table"], d["lens"], d["qs"],
+                            w.block_size, w.softmax_scale, d.get("ks"), d.get("vs"),
+                            requests=requests)
+
+
+def _rows(d, requests):
+    return np.concatenate([np.arange(d["qs"][b], d["qs"][b + 1]) for b in requests])
+
+
+def _err(out, ref, rows=None):
+    if rows is not None:
+        out, ref = out[rows], ref[rows]
+    assert np.all(np.isfinite(out)), "non-finite GPU output"
+    return float(np.max(np.abs(out - ref))) if out.size else 0.0
+
+
+# ---------------------------------------------------------------------------
+# append
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name,kw", [
+    ("tiny_chunks", {}),
+    ("tiny_chunks", dict(lens_after=[9, 18, 34, 5, 4], new_tokens=[7, 3, 0, 5, 4])),
+    ("llama8b", dict(lens_after=[40, 17, 33, 300], new_tokens=[20, 17, 2, 129], H_Q=8, H_KV=2)),
+    ("fp8_gqa", dict(lens_after=[40, 17, 33, 300], new_tokens=[20, 17, 2, 129], H_Q=8, H_KV=2)),
+    ("fp8_gqa", dict(lens_after=[40, 17], new_tokens=[23, 5], H_Q=8, H_KV=2, q_dtype="f32")),
+], ids=lambda x: str(x)[:40])
+def test_append_chunk_bit_exact(name, kw):
+    w = make_workload(name, **kw)
+    _log(f"append chunk {name} {kw}")
+    g = lambda t: t.to(DEV).contiguous()
+    kc, vc = g(w.k_cache[0]), g(w.v_cache[0])
+    ks = g(w.k_scale[0]) if w.k_scale else None
+    vs = g(w.v_scale[0]) if w.v_scale else None
+    pkv.kv_append_chunk(g(w.k_new[0]), g(w.v_new[0]), kc, vc, g(w.block_table),
+                        g(w.context_lens), g(w.query_start), ks, vs)
+    torch.cuda.synchronize()
+    d = _np(w)
+    rk, rv = paged.append_chunk(d["k_cache"], d["v_cache"], w.kv_dtype, d["k_new"], d["v_new"],
+                                w.q_dtype, d["table"], d["lens"], d["qs"], w.block_size,
+                                d.get("ks"), d.get("vs"))
+    assert np.array_equal(as_numpy(kc.cpu()), rk) and np.array_equal(as_numpy(vc.cpu()), rv)
+
+
+# ---------------------------------------------------------------------------
+# attention
+# ---------------------------------------------------------------------------
+
+def test_tiny_chunks_generic():
+    for kw in [{}, dict(lens_after=[9, 18, 34, 5, 4], new_tokens=[7, 3, 0, 5, 4])]:
+        w = make_workload("tiny_chunks", **kw)
+        _, _, out = gpu_chunk(w)
+        _, _, ref = oracle_chunk(w, _np(w))
+        e = _err(out, ref)
+        _log(f"tiny_chunks {kw} err={e:.2e}")
+        assert e <= TOL
+
+
+@pytest.mark.parametrize("variant", KERNELS, ids=KIDS)
+@pytest.mark.parametrize("hq_hkv", [(8, 8), (8, 4), (16, 4), (32, 8), (32, 2), (32, 1)])
+def test_chunk_group_sizes_bf16(variant, hq_hkv):
+    H_Q, H_KV = hq_hkv
+    w = make_workload("llama8b", lens_after=[40, 17, 300, 77, 1], new_tokens=[20, 17, 129, 1, 1],
+                      H_Q=H_Q, H_KV=H_KV)
+    _, _, out = gpu_chunk(w, variant)
+    _, _, ref = oracle_chunk(w, _np(w))
+    e = _err(out, ref)
+    _log(f"chunk g={H_Q // H_KV} variant={variant} err={e:.2e}")
+    assert e <= TOL
+
+
+@pytest.mark.parametrize("variant", KERNELS, ids=KIDS)
+def test_chunk_fp8(variant):
+    w = make_workload("fp8_gqa", lens_after=[40, 17, 300, 600], new_tokens=[20, 17, 129, 64],
+                      H_Q=32, H_KV=8)
+    _, _, out = gpu_chunk(w, variant)
+    _, _, ref = oracle_chunk(w, _np(w))
+    e = _err(out, ref)
+    _log(f"chunk fp8 variant={variant} err={e:.2e}")
+    assert e <= TOL
+
+
+def test_chunk_generic_other_head_dims():
+    for d_h, bs in [(64, 8), (80, 16), (256, 4), (12, 16)]:
+        w = make_workload("llama8b", lens_after=[40, 9, 33], new_tokens=[13, 9, 2], H_Q=8,
+                          H_KV=2, d_h=d_h, block_size=bs)
+        _, _, out = gpu_chunk(w)
+        _, _, ref = oracle_chunk(w, _np(w))
+        e = _err(out, ref)
+        _log(f"chunk d_h={d_h} bs={bs} err={e:.2e}")
+        assert e <= TOL
+
+
+@pytest.mark.parametrize("variant", KERNELS, ids=KIDS)
+def test_twelve_token_prompt_in_chunks_of_four(variant):
+    whole = make_workload("llama8b", lens_after=[12], new_tokens=[12], H_Q=8, H_KV=2)
+    kc_w, vc_w, out_w = gpu_chunk(whole, variant)
+    kc, vc = whole.k_cache[0], whole.v_cache[0]
+    parts = []
+    for c in range(3):
+        w = make_workload("llama8b", lens_after=[4 * c + 4], new_tokens=[4], H_Q=8, H_KV=2)
+        for name in ("q", "k_new", "v_new"):
+            getattr(w, name)[0] = getattr(whole, name)[0][4 * c:4 * c + 4].clone()
+        w.block_table = whole.block_table
+        kc, vc, o = gpu_chunk(w, variant, kc=kc, vc=vc)
+        parts.append(o)
+    assert torch.equal(kc, kc_w) and torch.equal(vc, vc_w)
+    assert np.max(np.abs(np.concatenate(parts) - out_w)) <= 1e-5
+    _, _, ref = oracle_chunk(whole, _np(whole))
+    assert _err(out_w, ref) <= TOL
+
+
+def test_one_token_chunks_agree_with_decode():
+    w = make_workload("llama8b", lens_after=[40, 17, 300, 1000], H_Q=32, H_KV=8)
+    assert w.total_q == w.B
+    _, _, out = gpu_chunk(w)
+    g = lambda t: t.to(DEV).contiguous()
+    kc, vc = g(w.k_cache[0]), g(w.v_cache[0])
+    bt, cl = g(w.block_table), g(w.context_lens)
+    pkv.kv_append(g(w.k_new[0]), g(w.v_new[0]), kc, vc, bt, cl)
+    _, _, ws = pkv.decode_plan(w.B, w.H_Q, w.H_KV, w.d_h, w.block_size, w.max_context_len)
+    work = torch.empty(max(ws, 256), dtype=torch.uint8, device=DEV)
+    dec = torch.empty((w.B, w.H_Q, w.d_h), dtype=torch.float32, device=DEV)
+    pkv.paged_decode_attention(dec, g(w.q[0]), kc, vc, bt, cl, w.max_context_len,
+                               w.softmax_scale, workspace=work)
+    torch.cuda.synchronize()
+    assert np.max(np.abs(out - dec.cpu().numpy())) <= TOL
+
+
+@pytest.mark.parametrize("variant", KERNELS, ids=KIDS)
+def test_chunk_unused_slots_never_read(variant):
+    w = make_workload("llama8b", lens_after=[40, 17, 33], new_tokens=[20, 17, 2], H_Q=8, H_KV=2)
+    d = _np(w)
+    _, _, ref = oracle_chunk(w, d)
+    kc, vc = w.k_cache[0].clone(), w.v_cache[0].clone()
+    used = set()
+    for b in range(w.B):
+        n = int(w.context_lens[b])
+        for t in range(n):
+            used.add((int(w.block_table[b, t // 16]), t % 16))
+    for p in range(w.num_blocks):
+        for r in range(16):
+            if (p, r) not in used:
+                kc[p, :, r] = float("nan")
+                vc[p, :, r] = float("nan")
+    _, _, out = gpu_chunk(w, variant, kc=kc, vc=vc)
+    assert _err(out, ref) <= TOL
+
+
+def test_prefix_hit_full_size_sampled():
+    w = make_workload("prefix_hit", device=DEV)
+    assert w.B == 64 and w.total_q == 38400 and w.shared_blocks == 75
+    _log("prefix_hit full size")
+    _, _, out = gpu_chunk(w)
+    d = _np(w)
+    req = [0, 37, 63]
+    _, _, ref = oracle_chunk(w, d, requests=req)
+    e = _err(out, ref, _rows(d, req))
+    _log(f"prefix_hit sampled err={e:.2e}")
+    assert e <= TOL
+    assert np.all(np.isfinite(out))
+
+
+def test_chunk_invalid_arguments_are_rejected():
+    w = make_workload("llama8b", lens_after=[40, 17], new_tokens=[20, 17], H_Q=8, H_KV=2)
+    g = lambda t: t.to(DEV).contiguous()
+    kc, vc, q = g(w.k_cache[0]), g(w.v_cache[0]), g(w.q[0])
+    bt, cl, qs = g(w.block_table), g(w.context_lens), g(w.query_start)
+    out = torch.empty((w.total_q, w.H_Q, w.d_h), dtype=torch.float32, device=DEV)
+    lib = pkv.load()
+    args = lambda **o: dict(dict(max_q_len=20, max_ctx=40, qsp=qs.data_ptr()), **o)
+
+    def call(max_q_len, max_ctx, qsp):
+        return lib.pkv_paged_chunk_attention(out.data_ptr(), q.data_ptr(), pkv.PKV_BF16,
+                                             kc.data_ptr(), vc.data_ptr(), pkv.PKV_BF16, None,
+                                             None, bt.data_ptr(), bt.shape[1], cl.data_ptr(),
+                                             qsp, w.B, w.total_q, max_q_len, max_ctx, w.H_Q,
+                                             w.H_KV, w.d_h, 16, w.num_blocks,
+                                             w.softmax_scale, None)
+    assert call(**args()) == 0
+    assert call(**args(max_q_len=0)) == -1
+    assert call(**args(max_q_len=41)) == -1
+    assert call(**args(qsp=None)) == -1
+    torch.cuda.synchronize()
