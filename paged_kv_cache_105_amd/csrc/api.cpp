@@ -31,8 +31,8 @@ hipError_t launch_decode_generic(int q_dtype, int kv_dtype, const DecodeArgs& a,
                                  hipStream_t stream);
 size_t generic_lds_bytes(int g, int d_h, int partition_tokens);
 bool mfma_supports(int q_dtype, int kv_dtype, int d_h, int block_size, int g);
-int mfma_flat_waves(int kv_dtype, int g, int depth, int B);
-hipError_t launch_decode_mfma(int kv_dtype, int depth, bool flat, int waves, const DecodeArgs& a,
+int mfma_flat_waves(int kv_dtype, int g, int B);
+hipError_t launch_decode_mfma(int kv_dtype, bool flat, int waves, const DecodeArgs& a,
                               hipStream_t stream);
 hipError_t launch_copy_blocks(void* k_cache, void* v_cache, float* k_scale, float* v_scale,
                               const int32_t* pairs, int n_pairs, size_t block_bytes, int H_KV,
@@ -45,17 +45,6 @@ hipError_t launch_combine(float* out, const int32_t* context_lens, const void* w
 namespace {
 
 int g_variant = PKV_VARIANT_AUTO;
-
-// Blocks the MFMA kernel keeps in flight ahead of the one it processes.
-// PKV_DECODE_DEPTH (1..3) overrides the default, for tuning measurements.
-int prefetch_depth() {
-  static const int depth = [] {
-    const char* e = std::getenv("PKV_DECODE_DEPTH");
-    const int d = e ? std::atoi(e) : 1;
-    return (d >= 1 && d <= 3) ? d : 1;
-  }();
-  return depth;
-}
 
 constexpr int kMaxDh = 256;
 constexpr int kMaxGenericPartition = 256;
@@ -97,20 +86,20 @@ struct Plan {
   size_t total;   // workspace bytes (0: none needed)
 };
 
-int flat_waves_cached(int kv_dtype, int g, int depth, int B) {
+int flat_waves_cached(int kv_dtype, int g, int B) {
   // the occupancy query depends on the kernel instance and its LDS size
   static std::mutex mu;
-  static std::map<std::tuple<int, int, int, int, int>, int> cache;
+  static std::map<std::tuple<int, int, int, int>, int> cache;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) {
     (void)hipGetLastError();
     dev = -1;
   }
-  const auto key = std::make_tuple(dev, kv_dtype, g > 16 ? 2 : 1, depth, B);
+  const auto key = std::make_tuple(dev, kv_dtype, g > 16 ? 2 : 1, B);
   std::lock_guard<std::mutex> lock(mu);
   auto it = cache.find(key);
   if (it != cache.end()) return it->second;
-  int w = pkv::mfma_flat_waves(kv_dtype, g, depth, B);
+  int w = pkv::mfma_flat_waves(kv_dtype, g, B);
   // PKV_FLAT_WAVES overrides the grid size of the balanced split, for tuning
   // measurements (more waves than fit at once only adds a second round)
   if (const char* e = std::getenv("PKV_FLAT_WAVES")) {
@@ -158,7 +147,7 @@ int make_plan(int B, int H_Q, int H_KV, int d_h, int block_size, int max_context
   if (plan->kernel == K_MFMA_PARTITION && pt > kMfmaMaxPartition) return PKV_ERR_UNSUPPORTED;
 
   if (plan->kernel == K_MFMA_FLAT) {
-    plan->waves = flat_waves_cached(kv_dtype, g, prefetch_depth(), B);
+    plan->waves = flat_waves_cached(kv_dtype, g, B);
     plan->total = pkv::flat_layout(B, plan->waves, g, d_h).total;
   } else if (plan->max_parts == 1) {
     plan->total = 0;
@@ -411,10 +400,10 @@ int pkv_decode_partitions(float* out, const void* q, int q_dtype, const void* k_
   const hipStream_t s = static_cast<hipStream_t>(stream);
   switch (plan.kernel) {
     case K_MFMA_FLAT:
-      e = pkv::launch_decode_mfma(kv_dtype, prefetch_depth(), true, plan.waves, a, s);
+      e = pkv::launch_decode_mfma(kv_dtype, true, plan.waves, a, s);
       break;
     case K_MFMA_PARTITION:
-      e = pkv::launch_decode_mfma(kv_dtype, prefetch_depth(), false, 0, a, s);
+      e = pkv::launch_decode_mfma(kv_dtype, false, 0, a, s);
       break;
     default:
       e = pkv::launch_decode_generic(q_dtype, kv_dtype, a, s);

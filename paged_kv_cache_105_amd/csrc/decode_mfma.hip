@@ -238,26 +238,20 @@ bool mfma_supports(int q_dtype, int kv_dtype, int d_h, int block_size, int g) {
 }
 
 namespace {
-template <int KV, int NG, int DEPTH>
+// Loads run one block ahead of the block being processed (measured best;
+// blocks are processed in pairs, so the distance must be odd).
+constexpr int kDepth = 1;
+
+template <int KV, int NG>
 const void* mfma_kernel_ptr(bool flat) {
-  return flat ? reinterpret_cast<const void*>(&decode_mfma_flat_kernel<KV, NG, DEPTH>)
-              : reinterpret_cast<const void*>(&decode_mfma_kernel<KV, NG, DEPTH>);
+  return flat ? reinterpret_cast<const void*>(&decode_mfma_flat_kernel<KV, NG, kDepth>)
+              : reinterpret_cast<const void*>(&decode_mfma_kernel<KV, NG, kDepth>);
 }
 
-const void* pick_kernel(int kv_dtype, int g, int depth, bool flat) {
+const void* pick_kernel(int kv_dtype, int g, bool flat) {
   const bool two = g > 16;
-#define PKV_PICK(KV, NG)                                   \
-  switch (depth) {                                         \
-    case 2: return mfma_kernel_ptr<KV, NG, 2>(flat);       \
-    case 3: return mfma_kernel_ptr<KV, NG, 3>(flat);       \
-    default: return mfma_kernel_ptr<KV, NG, 1>(flat);      \
-  }
-  if (kv_dtype == DT_BF16) {
-    if (two) { PKV_PICK(DT_BF16, 2) } else { PKV_PICK(DT_BF16, 1) }
-  } else {
-    if (two) { PKV_PICK(DT_FP8, 2) } else { PKV_PICK(DT_FP8, 1) }
-  }
-#undef PKV_PICK
+  if (kv_dtype == DT_BF16) return two ? mfma_kernel_ptr<DT_BF16, 2>(flat) : mfma_kernel_ptr<DT_BF16, 1>(flat);
+  return two ? mfma_kernel_ptr<DT_FP8, 2>(flat) : mfma_kernel_ptr<DT_FP8, 1>(flat);
 }
 }  // namespace
 
@@ -268,8 +262,8 @@ const void* pick_kernel(int kv_dtype, int g, int depth, bool flat) {
 // for the same matrix and softmax work, so they need every resident wave to
 // keep the memory busy.  (Measured on MI355X: bf16 W = 1024 vs 3072 is
 // 58 vs 65 us on the 8B-style batch; fp8 is best at full occupancy.)
-int mfma_flat_waves(int kv_dtype, int g, int depth, int B) {
-  const void* k = pick_kernel(kv_dtype, g, depth, true);
+int mfma_flat_waves(int kv_dtype, int g, int B) {
+  const void* k = pick_kernel(kv_dtype, g, true);
   int dev = 0, cus = 0, per_cu = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
@@ -284,9 +278,9 @@ int mfma_flat_waves(int kv_dtype, int g, int depth, int B) {
   return cus * per_cu;
 }
 
-hipError_t launch_decode_mfma(int kv_dtype, int depth, bool flat, int waves, const DecodeArgs& a,
+hipError_t launch_decode_mfma(int kv_dtype, bool flat, int waves, const DecodeArgs& a,
                               hipStream_t stream) {
-  const void* k = pick_kernel(kv_dtype, a.g, depth, flat);
+  const void* k = pick_kernel(kv_dtype, a.g, flat);
   void* args[] = {const_cast<DecodeArgs*>(&a)};
   if (flat) {
     return hipLaunchKernel(k, dim3(waves), dim3(64), args, sizeof(int32_t) * (a.B + 1), stream);

@@ -10,7 +10,8 @@
 // loads into all of them:
 //
 //   S[token][column] = K_blk[16 x 128] . Q^T[128 x 16]     (4 x MFMA 16x16x32)
-//   O^T[dim][column] += V_blk^T[128 x 16] . P^T[16 x 16]   (8 x 2 x MFMA 16x16x16)
+//   O^T[dim][column] += V_pair^T[128 x 32] . P^T[32 x 16]  (8 x 2 x MFMA 16x16x32
+//                                                           per pair of blocks)
 //
 // Lane l = 16 q + c (q = l / 16, c = l % 16).  Layouts:
 //   * A coalesced 1 KiB load s (s = 0..3) of a bf16 block gives lane l the
@@ -22,9 +23,12 @@
 //     Its result then gives lane l the scores of tokens q + 4i (i = 0..3)
 //     for column c -- exactly the B operand layout of the PV product with
 //     the same token permutation, so P never moves between lanes.
-//   * PV step n (n = 0..7) uses A-operand row c for dim 8c + n and k-index
-//     4q + i for token q + 4i: lane l already holds V[q + 4i][8c + n] from
-//     load s = i, so V needs one byte-permute per pair of values and no LDS.
+//   * PV runs once per pair of blocks (a, b), with K = 32: step n
+//     (n = 0..7) uses A-operand row c for dim 8c + n and k-index 8q + i for
+//     token q + 4i of block a (i < 4) or q + 4(i - 4) of block b (i >= 4):
+//     lane l already holds V[q + 4i][8c + n] of both blocks from load
+//     s = i, so V needs one byte-permute per pair of values and no LDS.
+//     (The K = 16 product runs at half the K = 32 product's rate on gfx950.)
 //   * The accumulator of step n gives lane l column c, dims 32q + 8i + n:
 //     every lane owns one column's running max and sum, and rescales its own
 //     accumulators.
@@ -173,18 +177,25 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
 }
 
-// One block of 16 positions: QK, online softmax, PV.  `valid` counts the
-// block's positions that hold cached entries (<= 0 for a padding step,
-// which leaves the state unchanged); V rows at or past it are zeroed.  A
-// score of this lane's column of group G counts only for tokens
-// <= lim[G] (block-relative); `full` (uniform) says that every column sees
-// all 16 tokens, so no score needs a mask.
+// Scores and V operands of one block, kept until its pair is complete.
+template <int NG>
+struct Half {
+  float s2[NG][4];  // scores of tokens q + 4i for this lane's column, log2 units
+  u32x4 vb[4];      // V: token 4s + q, dims 8c .. 8c + 7 (bf16 pairs)
+  float vscale;     // fp8 V scale of the block (1 for bf16)
+};
+
+// QK of one block of 16 positions.  `valid` counts the block's positions
+// that hold cached entries (<= 0 for a padding step); V rows at or past it
+// are zeroed.  A score of this lane's column of group G counts only for
+// tokens <= lim[G] (block-relative); `full` (uniform) says that every
+// column sees all 16 tokens, so no score needs a mask.  Masked scores are
+// -inf.
 template <int KV, int NG>
-__device__ __forceinline__ void process_block(float scale_log2, const LaneMap& L,
-                                              u32x4* lds_k, const bf16x8 (&qop)[NG][4],
-                                              Acc<NG>& acc, const Raw<KV>& kr,
-                                              const Raw<KV>& vr, int valid, bool full,
-                                              const int (&lim)[NG]) {
+__device__ __forceinline__ void qk_block(float scale_log2, const LaneMap& L, u32x4* lds_k,
+                                         const bf16x8 (&qop)[NG][4], const Raw<KV>& kr,
+                                         const Raw<KV>& vr, int valid, bool full,
+                                         const int (&lim)[NG], Half<NG>& out) {
   // ---- K: widen, transpose through LDS, QK on the matrix cores
 #pragma unroll
   for (int s = 0; s < 4; ++s) lds_k[L.wpos[s]] = as_bf16x8<KV>(kr, s);
@@ -194,39 +205,59 @@ __device__ __forceinline__ void process_block(float scale_log2, const LaneMap& L
   for (int j = 0; j < 4; ++j) ka[j] = __builtin_bit_cast(bf16x8, lds_k[L.rpos[j]]);
 
   float kscale = scale_log2;
-  float vscale = 1.0f;
+  out.vscale = 1.0f;
   if constexpr (KV == DT_FP8) {
     kscale *= kr.scale;
-    vscale = vr.scale;
+    out.vscale = vr.scale;
   }
-
   // ---- V operands: token q + 4i, dim 8c + n  (zero the invalid rows)
-  u32x4 vb[4];
 #pragma unroll
-  for (int s = 0; s < 4; ++s) vb[s] = as_bf16x8<KV>(vr, s);
+  for (int s = 0; s < 4; ++s) out.vb[s] = as_bf16x8<KV>(vr, s);
   if (valid < kBS) {
 #pragma unroll
     for (int s = 0; s < 4; ++s)
-      if (4 * s + L.q4 >= valid) vb[s] = u32x4{0u, 0u, 0u, 0u};
+      if (4 * s + L.q4 >= valid) out.vb[s] = u32x4{0u, 0u, 0u, 0u};
   }
-
 #pragma unroll
   for (int G = 0; G < NG; ++G) {
     f32x4 sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int j = 0; j < 4; ++j)
       sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[j], qop[G][j], sc, 0, 0, 0);
-
-    // online softmax for head 16G + c over tokens q + 4i
-    float s2[4];
 #pragma unroll
-    for (int ii = 0; ii < 4; ++ii) s2[ii] = sc[ii] * kscale;
+    for (int ii = 0; ii < 4; ++ii) out.s2[G][ii] = sc[ii] * kscale;
     if (!full) {
 #pragma unroll
       for (int ii = 0; ii < 4; ++ii)
-        if (L.q4 + 4 * ii > lim[G]) s2[ii] = -INFINITY;
+        if (L.q4 + 4 * ii > lim[G]) out.s2[G][ii] = -INFINITY;
     }
-    float mx = fmaxf(fmaxf(s2[0], s2[1]), fmaxf(s2[2], s2[3]));
+  }
+  // the K tile in LDS is rewritten by the next block: keep its reads first
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// Online softmax and PV over a pair of blocks (32 positions) with K = 32
+// products: MFMA k-index 8q + i is token q + 4i of block a for i < 4 and
+// token q + 4(i - 4) of block b for i >= 4, so each lane builds both
+// operands from what it holds.
+template <int NG>
+__device__ __forceinline__ void softmax_pv_pair(const Half<NG>& a, const Half<NG>& b,
+                                                Acc<NG>& acc) {
+  // V operands for the 8 dim groups: A row c = dim 8c + n
+  u32x4 va[8];
+#pragma unroll
+  for (int nn = 0; nn < 8; ++nn) {
+    const uint32_t sel = (nn & 1) ? 0x07060302u : 0x05040100u;
+    const int k = nn >> 1;
+    va[nn].x = __builtin_amdgcn_perm(a.vb[1][k], a.vb[0][k], sel);
+    va[nn].y = __builtin_amdgcn_perm(a.vb[3][k], a.vb[2][k], sel);
+    va[nn].z = __builtin_amdgcn_perm(b.vb[1][k], b.vb[0][k], sel);
+    va[nn].w = __builtin_amdgcn_perm(b.vb[3][k], b.vb[2][k], sel);
+  }
+#pragma unroll
+  for (int G = 0; G < NG; ++G) {
+    float mx = fmaxf(fmaxf(fmaxf(a.s2[G][0], a.s2[G][1]), fmaxf(a.s2[G][2], a.s2[G][3])),
+                     fmaxf(fmaxf(b.s2[G][0], b.s2[G][1]), fmaxf(b.s2[G][2], b.s2[G][3])));
     mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
     // raise the running max only when needed (uniform branch over the wave;
@@ -239,38 +270,36 @@ __device__ __forceinline__ void process_block(float scale_log2, const LaneMap& L
       for (int nn = 0; nn < 8; ++nn) acc.o[G][nn] *= alpha;
       acc.m[G] = m_new;
     }
-    float pr[4];
+    float pr[8];
 #pragma unroll
-    for (int ii = 0; ii < 4; ++ii) pr[ii] = __builtin_amdgcn_exp2f(s2[ii] - acc.m[G]);  // 0 if invalid
-    acc.l[G] += (pr[0] + pr[1]) + (pr[2] + pr[3]);
-
-    // probabilities (times the V scale) as hi + lo bf16 pairs
-    if constexpr (KV == DT_FP8) {
-#pragma unroll
-      for (int ii = 0; ii < 4; ++ii) pr[ii] *= vscale;
+    for (int ii = 0; ii < 4; ++ii) {
+      pr[ii] = __builtin_amdgcn_exp2f(a.s2[G][ii] - acc.m[G]);       // 0 if masked
+      pr[4 + ii] = __builtin_amdgcn_exp2f(b.s2[G][ii] - acc.m[G]);
     }
-    const uint32_t h01 = pack_bf16x2(pr[0], pr[1]), h23 = pack_bf16x2(pr[2], pr[3]);
-    const uint32_t l01 = pack_bf16x2(pr[0] - __uint_as_float(h01 << 16),
-                                     pr[1] - __uint_as_float(h01 & 0xffff0000u));
-    const uint32_t l23 = pack_bf16x2(pr[2] - __uint_as_float(h23 << 16),
-                                     pr[3] - __uint_as_float(h23 & 0xffff0000u));
-    const i16x4 ph = __builtin_bit_cast(i16x4, u32x2{h01, h23});
-    const i16x4 pl = __builtin_bit_cast(i16x4, u32x2{l01, l23});
-
+    acc.l[G] += ((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7]));
+    // probabilities (times the fp8 V scale) as hi + lo bf16 pairs
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) {
+      pr[ii] *= a.vscale;
+      pr[4 + ii] *= b.vscale;
+    }
+    u32x4 hi, lo;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t h = pack_bf16x2(pr[2 * k], pr[2 * k + 1]);
+      hi[k] = h;
+      lo[k] = pack_bf16x2(pr[2 * k] - __uint_as_float(h << 16),
+                          pr[2 * k + 1] - __uint_as_float(h & 0xffff0000u));
+    }
+    const bf16x8 ph = __builtin_bit_cast(bf16x8, hi);
+    const bf16x8 pl = __builtin_bit_cast(bf16x8, lo);
 #pragma unroll
     for (int nn = 0; nn < 8; ++nn) {
-      const uint32_t sel = (nn & 1) ? 0x07060302u : 0x05040100u;
-      const int k = nn >> 1;
-      u32x2 av;
-      av.x = __builtin_amdgcn_perm(vb[1][k], vb[0][k], sel);
-      av.y = __builtin_amdgcn_perm(vb[3][k], vb[2][k], sel);
-      const i16x4 va = __builtin_bit_cast(i16x4, av);
-      acc.o[G][nn] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, ph, acc.o[G][nn], 0, 0, 0);
-      acc.o[G][nn] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pl, acc.o[G][nn], 0, 0, 0);
+      const bf16x8 v8 = __builtin_bit_cast(bf16x8, va[nn]);
+      acc.o[G][nn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v8, ph, acc.o[G][nn], 0, 0, 0);
+      acc.o[G][nn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v8, pl, acc.o[G][nn], 0, 0, 0);
     }
   }
-  // the K tile in LDS is rewritten by the next block: keep its reads first
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
 // Blocks [jb, je) of KV head h of one request (table row `row`, cached
@@ -283,6 +312,8 @@ __device__ __forceinline__ void process_block(float scale_log2, const LaneMap& L
 // unconditionally: a load past the group's last block re-reads that block
 // (an L2 hit), and a padding step sees no valid position.  The number of
 // loads in flight -- and every wait count -- is then the same on every path.
+// DEPTH + 1 is even, so steps come in pairs: the even step keeps its
+// scores and V operands, the odd step completes the pair's softmax and PV.
 template <int KV, int NG, int DEPTH, bool NT = true>
 __device__ __forceinline__ void run_blocks(const DecodeArgs& a, const LaneMap& L, u32x4* lds_k,
                                            const bf16x8 (&qop)[NG][4], Acc<NG>& acc,
@@ -313,7 +344,9 @@ __device__ __forceinline__ void run_blocks(const DecodeArgs& a, const LaneMap& L
       // processed (that would shrink the distance they run ahead)
       __builtin_amdgcn_sched_barrier(0);
     };
+    static_assert((DEPTH + 1) % 2 == 0, "blocks are processed in pairs");
     const int nsteps = (nblk + DEPTH) / (DEPTH + 1) * (DEPTH + 1);
+    Half<NG> half[2];
 #pragma unroll
     for (int d = 0; d < DEPTH; ++d) issue(kbuf[d], vbuf[d], d);
     for (int i0 = 0; i0 < nsteps; i0 += DEPTH + 1) {
@@ -327,8 +360,10 @@ __device__ __forceinline__ void run_blocks(const DecodeArgs& a, const LaneMap& L
         int lim[NG];
 #pragma unroll
         for (int G = 0; G < NG; ++G) lim[G] = min(pcol[G] - t0, valid - 1);
-        process_block<KV, NG>(a.scale_log2, L, lds_k, qop, acc, kbuf[u], vbuf[u], valid, full,
-                              lim);
+        // even steps keep their scores; odd steps complete the pair
+        qk_block<KV, NG>(a.scale_log2, L, lds_k, qop, kbuf[u], vbuf[u], valid, full, lim,
+                         half[u & 1]);
+        if (u & 1) softmax_pv_pair<NG>(half[0], half[1], acc);
       }
     }
   }
