@@ -99,6 +99,17 @@ class BlockPool:
         self.refcount[b] = 1
         return b
 
+    def alloc_n(self, n: int) -> list:
+        """n blocks from the queue head, or none at all (OutOfBlocks) when
+        fewer are free: a request brought back from host memory needs all of
+        its blocks (page 3, "End-to-end flow": the victim resumes when blocks
+        free up)."""
+        if n < 0:
+            raise InvalidArg("n must be >= 0")
+        if n > len(self.free):
+            raise OutOfBlocks(f"{n} blocks needed, {len(self.free)} free")
+        return [self.alloc() for _ in range(n)]
+
     def _check(self, b: int):
         if not (0 <= b < self.num_blocks) or self.refcount[b] == 0:
             raise BadBlock(f"block {b} is not live")

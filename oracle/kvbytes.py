@@ -79,3 +79,13 @@ def unique_block_bytes(block_tables, context_lens, block_size: int,
         for j in range(blocks_for_tokens(int(n), block_size)):
             seen.add(int(row[j]))
     return len(seen) * bytes_per_block
+
+
+def transfer_floor_s(nbytes: int, bytes_per_s: float) -> float:
+    """Lower bound on the time to move ``nbytes`` between memory tiers at an
+    effective rate (page 2 "KV Cache Explained", section "What changes when KV
+    moves off the GPU": bytes divided by the link rate; staging, connector and
+    contention costs come on top)."""
+    if bytes_per_s <= 0:
+        raise ValueError("rate must be positive")
+    return nbytes / bytes_per_s

@@ -155,6 +155,72 @@ def copy_blocks(k_cache, v_cache, pairs, k_scale=None, v_scale=None):
     return kc, vc, ks, vs
 
 
+# ---- swap to host and back -------------------------------------------------
+#
+# Page 1, section 21.3: offloading moves retained cache state to another
+# memory tier (CPU memory) and a later operation brings the needed blocks
+# back; it changes placement and data movement, not which positions a query
+# reads.  Page 3, "End-to-end flow": a preempted request's blocks are swapped
+# to pinned host memory and copied back when blocks free up, instead of being
+# recomputed.  Page 2, section "What changes when KV moves off the GPU": the
+# byte count sets the transfer floor.
+#
+# Record of one block in the host buffer (the pages fix no format; this is
+# the layout both sides use): the block's K bytes (all KV heads, all slots,
+# [H_KV][bs][d_h] as stored), then its V bytes, then for fp8 caches the
+# block's K scales and V scales ([H_KV] float32 each); the record is padded
+# with unspecified bytes to a multiple of 256.
+
+SWAP_ALIGN = 256
+
+
+def swap_record_bytes(kv_dtype: str, H_KV: int, d_h: int, block_size: int) -> tuple:
+    """(bytes of one block's K (or V), bytes of one padded record)."""
+    elem = {F32: 4, BF16: 2, FP8: 1}[kv_dtype]
+    blk = H_KV * block_size * d_h * elem
+    rec = 2 * blk + (2 * H_KV * 4 if kv_dtype == FP8 else 0)
+    return blk, -(-rec // SWAP_ALIGN) * SWAP_ALIGN
+
+
+def swap_out(k_cache, v_cache, kv_dtype: str, blocks, k_scale=None, v_scale=None):
+    """Host records of the listed blocks, in list order: uint8 [n, record]
+    (padding bytes zero here; the library leaves them unspecified)."""
+    nb, H_KV, bs, d_h = k_cache.shape
+    blk, rec = swap_record_bytes(kv_dtype, H_KV, d_h, bs)
+    out = np.zeros((len(blocks), rec), dtype=np.uint8)
+    for i, b in enumerate(blocks):
+        if not 0 <= int(b) < nb:
+            raise ValueError(f"block id {b} outside the pool")
+        out[i, :blk] = np.ascontiguousarray(k_cache[b]).view(np.uint8).reshape(-1)
+        out[i, blk:2 * blk] = np.ascontiguousarray(v_cache[b]).view(np.uint8).reshape(-1)
+        if kv_dtype == FP8:
+            o = 2 * blk
+            out[i, o:o + 4 * H_KV] = np.asarray(k_scale[b], dtype="<f4").view(np.uint8)
+            out[i, o + 4 * H_KV:o + 8 * H_KV] = np.asarray(v_scale[b], dtype="<f4").view(np.uint8)
+    return out
+
+
+def swap_in(k_cache, v_cache, kv_dtype: str, blocks, records, k_scale=None, v_scale=None):
+    """Write record i into block blocks[i]; returns new (k, v, k_scale,
+    v_scale) arrays (the inputs are not modified)."""
+    kc, vc = np.array(k_cache, copy=True), np.array(v_cache, copy=True)
+    ks = None if k_scale is None else np.array(k_scale, copy=True)
+    vs = None if v_scale is None else np.array(v_scale, copy=True)
+    nb, H_KV, bs, d_h = kc.shape
+    blk, rec = swap_record_bytes(kv_dtype, H_KV, d_h, bs)
+    for i, b in enumerate(blocks):
+        if not 0 <= int(b) < nb:
+            raise ValueError(f"block id {b} outside the pool")
+        r = np.asarray(records[i], dtype=np.uint8)
+        kc[b] = r[:blk].view(kc.dtype).reshape(kc.shape[1:])
+        vc[b] = r[blk:2 * blk].view(vc.dtype).reshape(vc.shape[1:])
+        if kv_dtype == FP8:
+            o = 2 * blk
+            ks[b] = r[o:o + 4 * H_KV].view("<f4")
+            vs[b] = r[o + 4 * H_KV:o + 8 * H_KV].view("<f4")
+    return kc, vc, ks, vs
+
+
 def decode_stored(pool_slice, kv_dtype: str, scale=None) -> np.ndarray:
     """Stored scalars -> float64 values (exact)."""
     if kv_dtype == F32:

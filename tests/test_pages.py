@@ -101,3 +101,11 @@ def test_checkpoint_cached_positions():
     # selection does not append: the cache holds the processed prompt only
     assert g["cached_positions_at_first_selection"] == g["prompt_tokens"]
     assert kvbytes.blocks_for_tokens(g["prompt_tokens"], 4) == 2
+
+
+@pytest.mark.parametrize("case", GOLD["transfer_floor"])
+def test_transfer_floor_page_2(case):
+    t = kvbytes.transfer_floor_s(case["bytes"], case["bytes_per_s"])
+    assert round(t, case["digits"]) == case["seconds_rounded"]
+    # the 4 GiB is the 32,768-token prefix of the same page (Eq. 21.2)
+    assert case["bytes"] == kvbytes.payload_bytes(32, 1, 8, 32768, 128, 2)
