@@ -156,6 +156,53 @@ def host_prefix_identity(block_size: int, prompt_tokens: int = 32768, reps: int 
             "hashlib_chain_us": round(openssl_us, 1)}
 
 
+def swap_measurement(w, pool, k_scale, v_scale, stream, dev, reps: int = 5):
+    """Swap one layer of a 32,768-token request (2,048 blocks of 16) to
+    pinned host memory and back with the library's gather/scatter kernel,
+    next to the runtime's DMA copy of the same bytes; and the time these
+    rates give for the 4 GiB of all 32 layers, against the page's floors of
+    that transfer at 50 and 10 GB/s."""
+    import torch
+
+    import paged_kv_cache_105_amd as pkv
+    n = min(2048, w.num_blocks)
+    kc, vc = pool
+    blk, rec = pkv.swap_record_bytes(pkv.dtype_code(kc), w.H_KV, w.d_h, w.block_size)
+    ids = torch.arange(n, dtype=torch.int32, device=dev)
+    host = torch.empty(n * rec, dtype=torch.uint8, pin_memory=True)
+    staged = torch.empty(n * rec, dtype=torch.uint8, device=dev)
+    moved = n * 2 * blk + (n * 8 * w.H_KV if w.kv_dtype == "fp8_e4m3" else 0)
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    out_ms = timed(lambda: pkv.swap_out(kc, vc, ids, host, k_scale, v_scale, stream=stream))
+    in_ms = timed(lambda: pkv.swap_in(kc, vc, ids, host, k_scale, v_scale, stream=stream))
+    d2h_ms = timed(lambda: host.copy_(staged, non_blocking=True))
+    h2d_ms = timed(lambda: staged.copy_(host, non_blocking=True))
+    gbs = lambda nbytes, ms: round(nbytes / (ms * 1e-3) / 1e9, 2)
+    full = 32 * moved          # all 32 layers of the request
+    res = {"blocks": n, "bytes_per_layer": moved,
+           "swap_out_gbs": gbs(moved, out_ms), "swap_in_gbs": gbs(moved, in_ms),
+           "dma_d2h_gbs": gbs(n * rec, d2h_ms), "dma_h2d_gbs": gbs(n * rec, h2d_ms),
+           "all_layers_bytes": full,
+           "all_layers_out_s": round(32 * out_ms * 1e-3, 4),
+           "all_layers_in_s": round(32 * in_ms * 1e-3, 4),
+           "page_floor_s_at_50GBps": round(full / 50e9, 4),
+           "page_floor_s_at_10GBps": round(full / 10e9, 4)}
+    log(f"swap of {n} blocks ({moved} B per layer): out {res['swap_out_gbs']} GB/s, in "
+        f"{res['swap_in_gbs']} GB/s; DMA copy {res['dma_d2h_gbs']} / {res['dma_h2d_gbs']} GB/s")
+    return res
+
+
 def cpu_baseline(w, layer_tensors, budget_s: float):
     """Time the oracle (as it stands) on a bounded sample: the append of the
     whole batch, then attention request by request until ~budget_s."""
@@ -343,6 +390,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-blocks", type=int, default=0, metavar="N",
                     help="also time pkv_copy_blocks on N random disjoint block pairs")
+    ap.add_argument("--no-swap", action="store_true",
+                    help="skip the swap-to-host measurement")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="after the bench, copy a MIB-sized buffer 5 times (plain copy kernel "
                          "of known size, to scale HBM counters)")
@@ -493,6 +542,9 @@ def main():
         log(f"copy_blocks: {n} pairs x {blk} B x (K, V) in {cms * 1e3:.1f} us = "
             f"{ref['copy_blocks_gbs']} GB/s read+write")
 
+    swap = swap_measurement(w, pools[0][0], ks[0], vs[0], stream, dev) if not args.no_swap \
+        else None
+
     if args.calibrate_copy > 0:
         src = torch.ones(args.calibrate_copy * 2 ** 20 // 4, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
@@ -539,6 +591,7 @@ def main():
                      "avg_launch_us": round(kern_avg_ms * 1e3, 3)},
         "cpu_baseline": cpu,
         "host_prefix_identity": host_prefix_identity(w.block_size),
+        "swap_32k_request_layer": swap,
     }
     print(json.dumps(res), flush=True)
 

@@ -102,6 +102,11 @@ void pkv_pool_destroy(pkv_pool* pool);
 
 /* Pop the queue head, set its refcount to 1.  OUT_OF_BLOCKS if empty. */
 int pkv_pool_alloc(pkv_pool* pool, int32_t* block_id);
+/* Pop n blocks from the queue head into ids[0..n), each with refcount 1,
+ * or none at all: OUT_OF_BLOCKS (and no change) if fewer than n are free.
+ * For bringing a swapped-out request back, which needs all of its blocks
+ * (page 3 "xf_kv_cache", "End-to-end flow"). */
+int pkv_pool_alloc_n(pkv_pool* pool, int32_t n, int32_t* ids);
 /* Map a live block into one more table (section 21.5 step 3).  BAD_BLOCK
  * if the block is free or out of range. */
 int pkv_pool_incref(pkv_pool* pool, int32_t block_id);
@@ -357,6 +362,42 @@ int pkv_paged_chunk_attention(float* out, const void* q, int q_dtype, const void
                               int32_t max_q_len, int32_t max_context_len, int32_t H_Q,
                               int32_t H_KV, int32_t d_h, int32_t block_size, int32_t num_blocks,
                               float softmax_scale, pkv_stream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Swap to host memory and back (page 1 section 21.3: offloading moves
+ * retained cache state to CPU memory and brings the needed blocks back;
+ * page 3 "xf_kv_cache", "End-to-end flow": a preempted request's blocks go
+ * to pinned host memory and are copied back when it resumes; page 2
+ * "KV Cache Explained", section "What changes when KV moves off the GPU":
+ * bytes / link rate is the floor of such a transfer).
+ *
+ * Record i of a record buffer holds one block: its K bytes ([H_KV][bs][d_h]
+ * as stored, block_bytes of them), then its V bytes, then for FP8_E4M3 its
+ * K scales and V scales ([H_KV] float each); records are record_bytes
+ * apart (a multiple of 256), padding bytes untouched.  The buffer may be
+ * pinned host memory (hipHostMalloc, torch pin_memory) or device memory;
+ * pageable host memory is refused (INVALID_ARG).  The kernels read or write
+ * it directly; the call is asynchronous on `stream`, so the caller
+ * synchronises before reading a swapped-out buffer on the host, and may
+ * release or reuse the blocks as soon as later work on the same stream is
+ * what overwrites them.
+ * ---------------------------------------------------------------------- */
+
+/* Sizes of one block's K (or V) bytes and of one padded record. */
+int pkv_swap_record_bytes(int kv_dtype, int32_t H_KV, int32_t d_h, int32_t block_size,
+                          size_t* block_bytes, size_t* record_bytes);
+/* Copy blocks[0..n) (device int32) into records 0..n-1 of `records`.  A
+ * record whose block id is outside [0, num_blocks) is skipped. */
+int pkv_swap_out(const void* k_cache, const void* v_cache, int kv_dtype, const float* k_scale,
+                 const float* v_scale, const int32_t* blocks, int32_t n, int32_t H_KV,
+                 int32_t d_h, int32_t block_size, int32_t num_blocks, void* records,
+                 pkv_stream_t stream);
+/* Copy records 0..n-1 back into blocks[0..n) (typically new ids from
+ * pkv_pool_alloc_n); the request's table row then lists those ids in the
+ * same logical order. */
+int pkv_swap_in(void* k_cache, void* v_cache, int kv_dtype, float* k_scale, float* v_scale,
+                const int32_t* blocks, int32_t n, int32_t H_KV, int32_t d_h, int32_t block_size,
+                int32_t num_blocks, const void* records, pkv_stream_t stream);
 
 /* Kernel selection for the attention calls (process-wide, not
  * thread-safe).  AUTO uses the MFMA kernel with the balanced per-wave split

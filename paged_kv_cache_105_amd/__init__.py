@@ -18,7 +18,7 @@ from ._lib import (PKV_BF16, PKV_F32, PKV_FP8_E4M3, PKV_VARIANT_AUTO, PKV_VARIAN
 __all__ = ["kv_append", "copy_blocks", "decode_plan", "paged_decode_attention", "decode_partitions",
            "combine_partitions", "set_decode_variant", "BlockPool", "PkvError", "load",
            "prefix_root", "block_hashes", "DIGEST_BYTES", "kv_append_chunk",
-           "paged_chunk_attention",
+           "paged_chunk_attention", "swap_record_bytes", "swap_out", "swap_in",
            "PKV_F32", "PKV_BF16", "PKV_FP8_E4M3", "PKV_VARIANT_AUTO", "PKV_VARIANT_GENERIC",
            "PKV_VARIANT_MFMA", "PKV_VARIANT_MFMA_PARTITION", "dtype_code"]
 
@@ -130,6 +130,31 @@ def paged_chunk_attention(out, q, k_cache, v_cache, block_table, context_lens, q
           "pkv_paged_chunk_attention")
 
 
+def swap_record_bytes(kv_dtype: int, H_KV: int, d_h: int, block_size: int):
+    """pkv_swap_record_bytes -> (block_bytes, record_bytes)."""
+    blk, rec = C.c_size_t(), C.c_size_t()
+    check(load().pkv_swap_record_bytes(kv_dtype, H_KV, d_h, block_size, C.byref(blk),
+                                       C.byref(rec)), "pkv_swap_record_bytes")
+    return blk.value, rec.value
+
+
+def swap_out(k_cache, v_cache, blocks, records, k_scale=None, v_scale=None, stream=None):
+    """pkv_swap_out: blocks is a device int32 tensor [n]; records a pinned
+    host (or device) uint8 tensor of at least n * record_bytes."""
+    num_blocks, H_KV, bs, d_h = k_cache.shape
+    check(load().pkv_swap_out(_ptr(k_cache), _ptr(v_cache), _dtype_code(k_cache), _ptr(k_scale),
+                              _ptr(v_scale), _ptr(blocks), blocks.shape[0], H_KV, d_h, bs,
+                              num_blocks, _ptr(records), _stream(stream)), "pkv_swap_out")
+
+
+def swap_in(k_cache, v_cache, blocks, records, k_scale=None, v_scale=None, stream=None):
+    """pkv_swap_in: the inverse of swap_out, into the listed blocks."""
+    num_blocks, H_KV, bs, d_h = k_cache.shape
+    check(load().pkv_swap_in(_ptr(k_cache), _ptr(v_cache), _dtype_code(k_cache), _ptr(k_scale),
+                             _ptr(v_scale), _ptr(blocks), blocks.shape[0], H_KV, d_h, bs,
+                             num_blocks, _ptr(records), _stream(stream)), "pkv_swap_in")
+
+
 def copy_blocks(k_cache, v_cache, pairs, k_scale=None, v_scale=None, stream=None):
     """pkv_copy_blocks: pairs is a device int32 tensor [n, 2] of (src, dst)."""
     num_blocks, H_KV, bs, d_h = k_cache.shape
@@ -230,6 +255,11 @@ class BlockPool:
         b = C.c_int32()
         check(self._lib.pkv_pool_alloc(self._h, C.byref(b)), "pkv_pool_alloc")
         return b.value
+
+    def alloc_n(self, n: int) -> list:
+        ids = (C.c_int32 * max(1, n))()
+        check(self._lib.pkv_pool_alloc_n(self._h, n, ids), "pkv_pool_alloc_n")
+        return list(ids[:n])
 
     def incref(self, block: int):
         check(self._lib.pkv_pool_incref(self._h, block), "pkv_pool_incref")

@@ -33,6 +33,7 @@ SIGNATURES = {
     "pkv_pool_create": (C.c_int, [_i32, _i32, _pi32, C.POINTER(_vp)]),
     "pkv_pool_destroy": (None, [_vp]),
     "pkv_pool_alloc": (C.c_int, [_vp, _pi32]),
+    "pkv_pool_alloc_n": (C.c_int, [_vp, _i32, _pi32]),
     "pkv_pool_incref": (C.c_int, [_vp, _i32]),
     "pkv_pool_decref": (C.c_int, [_vp, _i32]),
     "pkv_pool_refcount": (C.c_int, [_vp, _i32, _pi32]),
@@ -70,6 +71,12 @@ SIGNATURES = {
     "pkv_paged_chunk_attention": (C.c_int, [_vp, _vp, C.c_int, _vp, _vp, C.c_int, _vp, _vp, _vp,
                                             _i32, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
                                             _i32, _i32, _i32, _f, _vp]),
+    "pkv_swap_record_bytes": (C.c_int, [C.c_int, _i32, _i32, _i32, C.POINTER(_sz),
+                                        C.POINTER(_sz)]),
+    "pkv_swap_out": (C.c_int, [_vp, _vp, C.c_int, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
+                               _vp, _vp]),
+    "pkv_swap_in": (C.c_int, [_vp, _vp, C.c_int, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
+                              _vp, _vp]),
     "pkv_set_decode_variant": (C.c_int, [C.c_int]),
 }
 

@@ -22,6 +22,10 @@ hipError_t launch_kv_append(int in_dtype, int kv_dtype, const void* k_new, const
                             int max_blocks_per_seq, const int32_t* context_lens,
                             const int32_t* query_start, int B, int rows, int H_KV, int d_h,
                             int block_size, int num_blocks, hipStream_t stream);
+hipError_t launch_swap(bool to_host, void* k_cache, void* v_cache, float* k_scale,
+                       float* v_scale, const int32_t* blocks, int n, size_t blk_bytes,
+                       size_t rec_bytes, int H_KV, int num_blocks, void* records,
+                       hipStream_t stream);
 bool chunk_mfma_supports(int q_dtype, int kv_dtype, int d_h, int block_size);
 hipError_t launch_chunk_mfma(int kv_dtype, int max_q_len, const DecodeArgs& a,
                              hipStream_t stream);
@@ -453,6 +457,88 @@ int pkv_paged_decode_attention(float* out, const void* q, int q_dtype, const voi
   return pkv_combine_partitions(out, context_lens, max_context_len, B, H_Q, H_KV, d_h,
                                 block_size, partition_tokens, workspace, workspace_bytes,
                                 stream);
+}
+
+int pkv_swap_record_bytes(int kv_dtype, int32_t H_KV, int32_t d_h, int32_t block_size,
+                          size_t* block_bytes, size_t* record_bytes) {
+  if (!valid_dtype(kv_dtype) || H_KV < 1 || d_h < 1 || d_h > kMaxDh || block_size < 1 ||
+      !record_bytes)
+    return PKV_ERR_INVALID_ARG;
+  const size_t elem = kv_dtype == PKV_F32 ? 4 : (kv_dtype == PKV_BF16 ? 2 : 1);
+  const size_t blk = static_cast<size_t>(H_KV) * block_size * d_h * elem;
+  const size_t rec = 2 * blk + (kv_dtype == PKV_FP8_E4M3 ? 2 * sizeof(float) * H_KV : 0);
+  if (block_bytes) *block_bytes = blk;
+  *record_bytes = (rec + 255) / 256 * 256;
+  return PKV_OK;
+}
+
+}  // extern "C"
+
+namespace {
+
+// Device address of a record buffer: device memory as is, pinned host
+// memory through its device mapping; anything else (pageable host memory)
+// is refused.
+int device_view(const void* p, void** out) {
+  hipPointerAttribute_t attr{};
+  if (hipPointerGetAttributes(&attr, p) != hipSuccess) {
+    (void)hipGetLastError();
+    return PKV_ERR_INVALID_ARG;
+  }
+  if (attr.type == hipMemoryTypeDevice) {
+    *out = const_cast<void*>(p);
+    return PKV_OK;
+  }
+  if (attr.type == hipMemoryTypeHost) {
+    void* d = nullptr;
+    if (hipHostGetDevicePointer(&d, const_cast<void*>(p), 0) != hipSuccess || !d) {
+      (void)hipGetLastError();
+      return PKV_ERR_INVALID_ARG;
+    }
+    *out = d;
+    return PKV_OK;
+  }
+  return PKV_ERR_INVALID_ARG;
+}
+
+int swap_common(bool to_host, void* k_cache, void* v_cache, int kv_dtype, float* k_scale,
+                float* v_scale, const int32_t* blocks, int32_t n, int32_t H_KV, int32_t d_h,
+                int32_t block_size, int32_t num_blocks, const void* records,
+                pkv_stream_t stream) {
+  if (!k_cache || !v_cache || !blocks || !records || n < 0 || num_blocks < 1)
+    return PKV_ERR_INVALID_ARG;
+  size_t blk = 0, rec = 0;
+  int st = pkv_swap_record_bytes(kv_dtype, H_KV, d_h, block_size, &blk, &rec);
+  if (st != PKV_OK) return st;
+  if (kv_dtype == PKV_FP8_E4M3 && (!k_scale || !v_scale)) return PKV_ERR_INVALID_ARG;
+  if (n == 0) return PKV_OK;
+  void* dev = nullptr;
+  st = device_view(records, &dev);
+  if (st != PKV_OK) return st;
+  const bool fp8 = kv_dtype == PKV_FP8_E4M3;
+  return hip_status(pkv::launch_swap(to_host, k_cache, v_cache, fp8 ? k_scale : nullptr,
+                                     fp8 ? v_scale : nullptr, blocks, n, blk, rec, H_KV,
+                                     num_blocks, dev, static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+extern "C" {
+
+int pkv_swap_out(const void* k_cache, const void* v_cache, int kv_dtype, const float* k_scale,
+                 const float* v_scale, const int32_t* blocks, int32_t n, int32_t H_KV,
+                 int32_t d_h, int32_t block_size, int32_t num_blocks, void* records,
+                 pkv_stream_t stream) {
+  return swap_common(true, const_cast<void*>(k_cache), const_cast<void*>(v_cache), kv_dtype,
+                     const_cast<float*>(k_scale), const_cast<float*>(v_scale), blocks, n, H_KV,
+                     d_h, block_size, num_blocks, records, stream);
+}
+
+int pkv_swap_in(void* k_cache, void* v_cache, int kv_dtype, float* k_scale, float* v_scale,
+                const int32_t* blocks, int32_t n, int32_t H_KV, int32_t d_h, int32_t block_size,
+                int32_t num_blocks, const void* records, pkv_stream_t stream) {
+  return swap_common(false, k_cache, v_cache, kv_dtype, k_scale, v_scale, blocks, n, H_KV, d_h,
+                     block_size, num_blocks, records, stream);
 }
 
 }  // extern "C"

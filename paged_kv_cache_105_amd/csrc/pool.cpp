@@ -169,6 +169,13 @@ int pkv_pool_alloc(pkv_pool* pool, int32_t* block_id) {
   return PKV_OK;
 }
 
+int pkv_pool_alloc_n(pkv_pool* pool, int32_t n, int32_t* ids) {
+  if (!pool || n < 0 || (n > 0 && !ids)) return PKV_ERR_INVALID_ARG;
+  if (n > pool->count) return PKV_ERR_OUT_OF_BLOCKS;
+  for (int32_t i = 0; i < n; ++i) ids[i] = pool->take_head();
+  return PKV_OK;
+}
+
 int pkv_pool_incref(pkv_pool* pool, int32_t block_id) {
   if (!pool) return PKV_ERR_INVALID_ARG;
   if (!pool->live(block_id)) return PKV_ERR_BAD_BLOCK;

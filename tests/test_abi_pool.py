@@ -198,3 +198,29 @@ def test_library_pool_matches_oracle_model_on_random_ops(seed):
             lib_pool.release(s[0], s[1])
         assert lib_pool.free_queue() == list(ref.free)
         assert [lib_pool.refcount(b) for b in range(nb)] == ref.refcount
+
+
+def test_swap_record_bytes_match_oracle():
+    from oracle import paged
+    codes = {"f32": pkv.PKV_F32, "bf16": pkv.PKV_BF16, "fp8_e4m3": pkv.PKV_FP8_E4M3}
+    for kv in codes:
+        for H_KV, d_h, bs in [(8, 128, 16), (1, 8, 4), (3, 12, 5), (32, 256, 1), (1, 1, 1)]:
+            assert pkv.swap_record_bytes(codes[kv], H_KV, d_h, bs) == \
+                paged.swap_record_bytes(kv, H_KV, d_h, bs)
+    with pytest.raises(pkv.PkvError):
+        pkv.swap_record_bytes(pkv.PKV_BF16, 0, 128, 16)
+
+
+def test_alloc_n_matches_oracle():
+    order = [7, 2, 9, 5, 0, 1, 3, 4, 6, 8]
+    lib, ref = pkv.BlockPool(10, 4, order), blockpool.BlockPool(10, 4, order)
+    assert lib.alloc_n(3) == ref.alloc_n(3) == [7, 2, 9]
+    with pytest.raises(pkv.PkvError) as e:
+        lib.alloc_n(8)
+    assert e.value.name == "out_of_blocks"
+    assert lib.free_queue() == [5, 0, 1, 3, 4, 6, 8]
+    assert lib.alloc_n(0) == []
+    lib.release((C.c_int32 * 3)(7, 2, 9), 3)
+    ref.release([7, 2, 9])
+    assert lib.alloc_n(10) == ref.alloc_n(10)
+    assert lib.num_free() == 0
