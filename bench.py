@@ -1,8 +1,9 @@
 """Benchmark of one paged decode step on one MI355X.
 
-A step is the whole hot path for one batch: kv_append of every request's
-new K/V, then paged decode attention (partition kernel + split-K combine)
-for one layer (or every layer of the ``shared_prefix`` workload).  Inputs are
+A step is the whole hot path for one batch: the append of every request's
+new K/V and paged decode attention (pkv_decode_step: the partition kernel,
+which also performs the append, + split-K combine) for one layer (or every
+layer of the ``shared_prefix`` workload).  Inputs are
 seeded synthetic draws resident in HBM before the timed region.  To keep the
 256 MB last-level cache from serving repeated reads, single-layer workloads
 rotate over ``--rotate`` copies of the KV pools (same tables, different
@@ -437,16 +438,13 @@ def main():
     vs = w.v_scale or [None] * w.layers
 
     def step(r):
+        # append + attention (+ combine): the append runs inside the attention
+        # launch where the MFMA kernels apply
         for L in range(w.layers):
             kc, vc = pools[r][L]
-            pkv.kv_append(w.k_new[L], w.v_new[L], kc, vc, w.block_table, w.context_lens,
-                          ks[L], vs[L], stream=stream)
-            pkv.decode_partitions(out, w.q[L], kc, vc, w.block_table, w.context_lens,
-                                  w.max_context_len, w.softmax_scale, ks[L], vs[L],
-                                  partition_tokens=pt, workspace=work, stream=stream)
-            pkv.combine_partitions(out, w.context_lens, w.max_context_len, w.H_KV,
-                                   w.block_size, partition_tokens=pt, workspace=work,
-                                   stream=stream)
+            pkv.decode_step(w.k_new[L], w.v_new[L], out, w.q[L], kc, vc, w.block_table,
+                            w.context_lens, w.max_context_len, w.softmax_scale, ks[L], vs[L],
+                            partition_tokens=pt, workspace=work, stream=stream)
 
     for i in range(args.warmup):
         step(i % R)

@@ -296,6 +296,21 @@ int pkv_paged_decode_attention(float* out, const void* q, int q_dtype, const voi
                                float softmax_scale, int32_t partition_tokens, void* workspace,
                                size_t workspace_bytes, pkv_stream_t stream);
 
+/* One decode step: pkv_kv_append of k_new / v_new ([B][H_KV][d_h] in the
+ * query dtype) followed by pkv_paged_decode_attention, same arguments and
+ * results (the pools end up byte for byte as after pkv_kv_append; k_cache
+ * and v_cache are written).  Where the MFMA kernels run on a bf16 cache
+ * with H_Q / H_KV <= 16, the append is done inside the attention launch by the wave that reads the
+ * request's last block, which uses the new row from registers (one launch
+ * fewer); other cases launch the append kernel first. */
+int pkv_decode_step(const void* k_new, const void* v_new, float* out, const void* q, int q_dtype,
+                    void* k_cache, void* v_cache, int kv_dtype, const float* k_scale,
+                    const float* v_scale, const int32_t* block_table, int32_t max_blocks_per_seq,
+                    const int32_t* context_lens, int32_t max_context_len, int32_t B, int32_t H_Q,
+                    int32_t H_KV, int32_t d_h, int32_t block_size, int32_t num_blocks,
+                    float softmax_scale, int32_t partition_tokens, void* workspace,
+                    size_t workspace_bytes, pkv_stream_t stream);
+
 /* The two launches of pkv_paged_decode_attention, callable separately (for
  * timing each kernel).  decode_partitions runs the online softmax over each
  * piece (same arguments); it writes `out` directly for requests whose

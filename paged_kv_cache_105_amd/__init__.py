@@ -18,7 +18,7 @@ from ._lib import (PKV_BF16, PKV_F32, PKV_FP8_E4M3, PKV_VARIANT_AUTO, PKV_VARIAN
 __all__ = ["kv_append", "copy_blocks", "decode_plan", "paged_decode_attention", "decode_partitions",
            "combine_partitions", "set_decode_variant", "BlockPool", "PkvError", "load",
            "prefix_root", "block_hashes", "DIGEST_BYTES", "kv_append_chunk",
-           "paged_chunk_attention", "swap_record_bytes", "swap_out", "swap_in",
+           "paged_chunk_attention", "swap_record_bytes", "swap_out", "swap_in", "decode_step",
            "PKV_F32", "PKV_BF16", "PKV_FP8_E4M3", "PKV_VARIANT_AUTO", "PKV_VARIANT_GENERIC",
            "PKV_VARIANT_MFMA", "PKV_VARIANT_MFMA_PARTITION", "dtype_code"]
 
@@ -195,6 +195,15 @@ def paged_decode_attention(out, q, k_cache, v_cache, block_table, context_lens,
     check(load().pkv_paged_decode_attention(*_attn_args(
         out, q, k_cache, v_cache, block_table, context_lens, max_context_len, softmax_scale,
         k_scale, v_scale, partition_tokens, workspace, stream)), "pkv_paged_decode_attention")
+
+
+def decode_step(k_new, v_new, out, q, k_cache, v_cache, block_table, context_lens,
+                max_context_len, softmax_scale, k_scale=None, v_scale=None, partition_tokens=0,
+                workspace=None, stream=None):
+    """pkv_decode_step: append k_new / v_new [B, H_KV, d_h], then attend."""
+    check(load().pkv_decode_step(_ptr(k_new), _ptr(v_new), *_attn_args(
+        out, q, k_cache, v_cache, block_table, context_lens, max_context_len, softmax_scale,
+        k_scale, v_scale, partition_tokens, workspace, stream)), "pkv_decode_step")
 
 
 def decode_partitions(out, q, k_cache, v_cache, block_table, context_lens, max_context_len,

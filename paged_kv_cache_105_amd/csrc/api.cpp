@@ -35,6 +35,7 @@ hipError_t launch_decode_generic(int q_dtype, int kv_dtype, const DecodeArgs& a,
                                  hipStream_t stream);
 size_t generic_lds_bytes(int g, int d_h, int partition_tokens);
 bool mfma_supports(int q_dtype, int kv_dtype, int d_h, int block_size, int g);
+bool mfma_fuses_append(int kv_dtype, int g);
 int mfma_flat_waves(int kv_dtype, int g, int B);
 hipError_t launch_decode_mfma(int kv_dtype, bool flat, int waves, const DecodeArgs& a,
                               hipStream_t stream);
@@ -357,14 +358,19 @@ int pkv_decode_plan(int32_t B, int32_t H_Q, int32_t H_KV, int32_t d_h, int32_t b
   return PKV_OK;
 }
 
-int pkv_decode_partitions(float* out, const void* q, int q_dtype, const void* k_cache,
-                          const void* v_cache, int kv_dtype, const float* k_scale,
-                          const float* v_scale, const int32_t* block_table,
-                          int32_t max_blocks_per_seq, const int32_t* context_lens,
-                          int32_t max_context_len, int32_t B, int32_t H_Q, int32_t H_KV,
-                          int32_t d_h, int32_t block_size, int32_t num_blocks,
-                          float softmax_scale, int32_t partition_tokens, void* workspace,
-                          size_t workspace_bytes, pkv_stream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// The partition launch; with k_new / v_new set (MFMA kernels only) the
+// owning waves also append the new token (see pkv_decode_step).
+int decode_launch(const void* k_new, const void* v_new, float* out, const void* q, int q_dtype,
+                  const void* k_cache, const void* v_cache, int kv_dtype, const float* k_scale,
+                  const float* v_scale, const int32_t* block_table, int32_t max_blocks_per_seq,
+                  const int32_t* context_lens, int32_t max_context_len, int32_t B, int32_t H_Q,
+                  int32_t H_KV, int32_t d_h, int32_t block_size, int32_t num_blocks,
+                  float softmax_scale, int32_t partition_tokens, void* workspace,
+                  size_t workspace_bytes, pkv_stream_t stream) {
   int st = check_attention_args(out, q, q_dtype, k_cache, v_cache, kv_dtype, k_scale, v_scale,
                                 block_table, max_blocks_per_seq, context_lens, max_context_len,
                                 B, H_Q, H_KV, d_h, block_size, num_blocks, softmax_scale);
@@ -399,6 +405,11 @@ int pkv_decode_partitions(float* out, const void* q, int q_dtype, const void* k_
   a.partition_tokens = plan.partition_tokens;
   a.max_parts = plan.max_parts;
   a.scale_log2 = softmax_scale * pkv::kLog2e;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  if (k_new && (!pkv::mfma_fuses_append(kv_dtype, H_Q / H_KV) ||
+                (plan.kernel != K_MFMA_FLAT && plan.kernel != K_MFMA_PARTITION)))
+    return PKV_ERR_UNSUPPORTED;
 
   hipError_t e;
   const hipStream_t s = static_cast<hipStream_t>(stream);
@@ -413,6 +424,25 @@ int pkv_decode_partitions(float* out, const void* q, int q_dtype, const void* k_
       e = pkv::launch_decode_generic(q_dtype, kv_dtype, a, s);
   }
   return hip_status(e);
+}
+
+
+}  // namespace
+
+extern "C" {
+
+int pkv_decode_partitions(float* out, const void* q, int q_dtype, const void* k_cache,
+                          const void* v_cache, int kv_dtype, const float* k_scale,
+                          const float* v_scale, const int32_t* block_table,
+                          int32_t max_blocks_per_seq, const int32_t* context_lens,
+                          int32_t max_context_len, int32_t B, int32_t H_Q, int32_t H_KV,
+                          int32_t d_h, int32_t block_size, int32_t num_blocks,
+                          float softmax_scale, int32_t partition_tokens, void* workspace,
+                          size_t workspace_bytes, pkv_stream_t stream) {
+  return decode_launch(nullptr, nullptr, out, q, q_dtype, k_cache, v_cache, kv_dtype, k_scale,
+                       v_scale, block_table, max_blocks_per_seq, context_lens, max_context_len, B,
+                       H_Q, H_KV, d_h, block_size, num_blocks, softmax_scale, partition_tokens,
+                       workspace, workspace_bytes, stream);
 }
 
 int pkv_combine_partitions(float* out, const int32_t* context_lens, int32_t max_context_len,
@@ -454,6 +484,45 @@ int pkv_paged_decode_attention(float* out, const void* q, int q_dtype, const voi
                  kv_dtype, &plan);
   if (st != PKV_OK) return st;
   if (plan.total == 0) return PKV_OK;  // one partition per request: out is final
+  return pkv_combine_partitions(out, context_lens, max_context_len, B, H_Q, H_KV, d_h,
+                                block_size, partition_tokens, workspace, workspace_bytes,
+                                stream);
+}
+
+int pkv_decode_step(const void* k_new, const void* v_new, float* out, const void* q, int q_dtype,
+                    void* k_cache, void* v_cache, int kv_dtype, const float* k_scale,
+                    const float* v_scale, const int32_t* block_table, int32_t max_blocks_per_seq,
+                    const int32_t* context_lens, int32_t max_context_len, int32_t B, int32_t H_Q,
+                    int32_t H_KV, int32_t d_h, int32_t block_size, int32_t num_blocks,
+                    float softmax_scale, int32_t partition_tokens, void* workspace,
+                    size_t workspace_bytes, pkv_stream_t stream) {
+  int st = check_attention_args(out, q, q_dtype, k_cache, v_cache, kv_dtype, k_scale, v_scale,
+                                block_table, max_blocks_per_seq, context_lens, max_context_len,
+                                B, H_Q, H_KV, d_h, block_size, num_blocks, softmax_scale);
+  if (st != PKV_OK) return st;
+  st = check_append_args(k_new, v_new, q_dtype, k_cache, v_cache, kv_dtype, k_scale, v_scale,
+                         block_table, max_blocks_per_seq, context_lens, B, H_KV, d_h,
+                         block_size, num_blocks);
+  if (st != PKV_OK) return st;
+  Plan plan;
+  st = make_plan(B, H_Q, H_KV, d_h, block_size, max_context_len, partition_tokens, q_dtype,
+                 kv_dtype, &plan);
+  if (st != PKV_OK) return st;
+  const bool aligned =
+      ((reinterpret_cast<uintptr_t>(k_new) | reinterpret_cast<uintptr_t>(v_new)) & 15) == 0;
+  const bool fused = aligned && pkv::mfma_fuses_append(kv_dtype, H_Q / H_KV) &&
+                     (plan.kernel == K_MFMA_FLAT || plan.kernel == K_MFMA_PARTITION);
+  if (!fused) {
+    st = pkv_kv_append(k_new, v_new, q_dtype, k_cache, v_cache, kv_dtype, k_scale, v_scale,
+                       block_table, max_blocks_per_seq, context_lens, B, H_KV, d_h, block_size,
+                       num_blocks, stream);
+    if (st != PKV_OK) return st;
+  }
+  st = decode_launch(fused ? k_new : nullptr, fused ? v_new : nullptr, out, q, q_dtype, k_cache,
+                     v_cache, kv_dtype, k_scale, v_scale, block_table, max_blocks_per_seq,
+                     context_lens, max_context_len, B, H_Q, H_KV, d_h, block_size, num_blocks,
+                     softmax_scale, partition_tokens, workspace, workspace_bytes, stream);
+  if (st != PKV_OK || plan.total == 0) return st;
   return pkv_combine_partitions(out, context_lens, max_context_len, B, H_Q, H_KV, d_h,
                                 block_size, partition_tokens, workspace, workspace_bytes,
                                 stream);

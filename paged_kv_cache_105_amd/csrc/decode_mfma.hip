@@ -38,6 +38,36 @@ __device__ __forceinline__ void load_q(const DecodeArgs& a, const LaneMap& L, in
   }
 }
 
+// The append fused into the attention launch (pkv_decode_step, bf16
+// caches): the wave whose blocks [jb, je) of sequence (b, h) include the
+// request's last position t = n - 1 loads the new K and V rows when it
+// starts the sequence; run_blocks stores them into their slot -- a bit
+// copy, the stored form of pkv_kv_append -- and uses them in place of the
+// slot's old contents when it reaches that block, so the attention reads
+// the new row without waiting for its own store.  Like pkv_kv_append it
+// does nothing for a request whose length or block id is out of range.
+__device__ __forceinline__ NewRow load_new_row(const DecodeArgs& a, const LaneMap& L, int b,
+                                               int h, const int32_t* row, int jb, int je) {
+  NewRow nr;
+  nr.blk = -1;
+  nr.slot = 0;
+  const int n = a.context_lens[b];
+  if (n < 1 || n > a.max_blocks_per_seq * kBS) return nr;
+  const int jn = (n - 1) / kBS;
+  if (jn < jb || jn >= je) return nr;
+  const int p = row[jn];
+  if (p < 0 || p >= a.num_blocks) return nr;
+  nr.blk = jn;
+  nr.slot = (n - 1) % kBS;
+  const size_t src = (static_cast<size_t>(b) * a.H_KV + h) * kD + 8 * L.c;
+  nr.k = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.k_new) + src);
+  nr.v = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.v_new) + src);
+  const size_t dst = ((static_cast<size_t>(p) * a.H_KV + h) * kBS + nr.slot) * kD + 8 * L.c;
+  nr.k_dst = reinterpret_cast<u32x4*>(static_cast<uint16_t*>(const_cast<void*>(a.k_cache)) + dst);
+  nr.v_dst = reinterpret_cast<u32x4*>(static_cast<uint16_t*>(const_cast<void*>(a.v_cache)) + dst);
+  return nr;
+}
+
 // Write the state: normalised output when `final_out` is set, else the
 // unnormalised partial (o, then (m, l) per head) with the given per-head
 // strides.  Lane l holds head 16G + c, dims 32q + 8i + n.
@@ -78,7 +108,7 @@ __device__ __forceinline__ void write_state(const Acc<NG>& acc, const LaneMap& L
 }
 
 // Partition mode: one wave per (partition, KV head, request).
-template <int KV, int NG, int DEPTH>
+template <int KV, int NG, int DEPTH, bool FUSED>
 __global__ __launch_bounds__(64, 2) void decode_mfma_kernel(DecodeArgs a) {
   __shared__ u32x4 lds_k[kBS * 16];  // 16 token rows x 16 chunks of 16 B
   const LaneMap L = lane_map();
@@ -106,8 +136,10 @@ __global__ __launch_bounds__(64, 2) void decode_mfma_kernel(DecodeArgs a) {
   int pcol[NG];
 #pragma unroll
   for (int G = 0; G < NG; ++G) pcol[G] = t1 - 1;
-  run_blocks<KV, NG, DEPTH>(a, L, lds_k, qop, acc, row, t1, h, t0 / kBS,
-                            (t1 + kBS - 1) / kBS, t1 - 1, pcol);
+  NewRow nr;
+  if constexpr (FUSED) nr = load_new_row(a, L, b, h, row, t0 / kBS, (t1 + kBS - 1) / kBS);
+  run_blocks<KV, NG, DEPTH, true, FUSED>(a, L, lds_k, qop, acc, row, t1, h, t0 / kBS,
+                                         (t1 + kBS - 1) / kBS, t1 - 1, pcol, &nr);
 
   const size_t hq0 = static_cast<size_t>(b) * a.H_Q + static_cast<size_t>(h) * a.g;
   if (nparts == 1) {
@@ -130,7 +162,7 @@ __global__ __launch_bounds__(64, 2) void decode_mfma_kernel(DecodeArgs a) {
 // sequences it overlaps: a sequence inside the chunk is written final, a cut
 // one as a partial in slot 0 (the chunk's first sequence) or slot 1 (its
 // last).
-template <int KV, int NG, int DEPTH>
+template <int KV, int NG, int DEPTH, bool FUSED>
 __global__ __launch_bounds__(64, 2) void decode_mfma_flat_kernel(DecodeArgs a) {
   __shared__ u32x4 lds_k[kBS * 16];
   extern __shared__ int32_t prefix[];  // [B + 1]
@@ -209,8 +241,12 @@ __global__ __launch_bounds__(64, 2) void decode_mfma_flat_kernel(DecodeArgs a) {
     int pcol[NG];
 #pragma unroll
     for (int G = 0; G < NG; ++G) pcol[G] = n - 1;
-    run_blocks<KV, NG, DEPTH>(a, L, lds_k, qop, acc, row, n, h, static_cast<int>(cur - S),
-                              static_cast<int>(pe - S), n - 1, pcol);
+    NewRow nr;
+    if constexpr (FUSED)
+      nr = load_new_row(a, L, b, h, row, static_cast<int>(cur - S), static_cast<int>(pe - S));
+    run_blocks<KV, NG, DEPTH, true, FUSED>(a, L, lds_k, qop, acc, row, n, h,
+                                           static_cast<int>(cur - S), static_cast<int>(pe - S),
+                                           n - 1, pcol, &nr);
     const size_t hq0 = static_cast<size_t>(b) * a.H_Q + static_cast<size_t>(h) * a.g;
     if (S >= lo && E <= hi) {
       write_state<NG>(acc, L, a.g, a.out + hq0 * kD, nullptr, 0, nullptr, 0);
@@ -232,6 +268,12 @@ __global__ __launch_bounds__(64, 2) void decode_mfma_flat_kernel(DecodeArgs a) {
   }
 }
 
+// The fused append keeps the new row in registers for the whole walk: with
+// bf16 caches and one head group that fits (the bf16 kernel runs one wave
+// per SIMD anyway); fp8 would lose a wave per SIMD and two head groups
+// would spill, so those cases launch the append kernel first.
+bool mfma_fuses_append(int kv_dtype, int g) { return kv_dtype == DT_BF16 && g <= 16; }
+
 bool mfma_supports(int q_dtype, int kv_dtype, int d_h, int block_size, int g) {
   return q_dtype == DT_BF16 && (kv_dtype == DT_BF16 || kv_dtype == DT_FP8) && d_h == kD &&
          block_size == kBS && g >= 1 && g <= 32;
@@ -242,15 +284,20 @@ namespace {
 // blocks are processed in pairs, so the distance must be odd).
 constexpr int kDepth = 1;
 
-template <int KV, int NG>
+template <int KV, int NG, bool FUSED = false>
 const void* mfma_kernel_ptr(bool flat) {
-  return flat ? reinterpret_cast<const void*>(&decode_mfma_flat_kernel<KV, NG, kDepth>)
-              : reinterpret_cast<const void*>(&decode_mfma_kernel<KV, NG, kDepth>);
+  return flat ? reinterpret_cast<const void*>(&decode_mfma_flat_kernel<KV, NG, kDepth, FUSED>)
+              : reinterpret_cast<const void*>(&decode_mfma_kernel<KV, NG, kDepth, FUSED>);
 }
 
-const void* pick_kernel(int kv_dtype, int g, bool flat) {
+// fused: the append runs inside the launch (bf16 caches, one head group;
+// see mfma_fuses_append)
+const void* pick_kernel(int kv_dtype, int g, bool flat, bool fused) {
   const bool two = g > 16;
-  if (kv_dtype == DT_BF16) return two ? mfma_kernel_ptr<DT_BF16, 2>(flat) : mfma_kernel_ptr<DT_BF16, 1>(flat);
+  if (kv_dtype == DT_BF16) {
+    if (fused && !two) return mfma_kernel_ptr<DT_BF16, 1, true>(flat);
+    return two ? mfma_kernel_ptr<DT_BF16, 2>(flat) : mfma_kernel_ptr<DT_BF16, 1>(flat);
+  }
   return two ? mfma_kernel_ptr<DT_FP8, 2>(flat) : mfma_kernel_ptr<DT_FP8, 1>(flat);
 }
 }  // namespace
@@ -263,7 +310,7 @@ const void* pick_kernel(int kv_dtype, int g, bool flat) {
 // keep the memory busy.  (Measured on MI355X: bf16 W = 1024 vs 3072 is
 // 58 vs 65 us on the 8B-style batch; fp8 is best at full occupancy.)
 int mfma_flat_waves(int kv_dtype, int g, int B) {
-  const void* k = pick_kernel(kv_dtype, g, true);
+  const void* k = pick_kernel(kv_dtype, g, true, false);
   int dev = 0, cus = 0, per_cu = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
@@ -280,7 +327,7 @@ int mfma_flat_waves(int kv_dtype, int g, int B) {
 
 hipError_t launch_decode_mfma(int kv_dtype, bool flat, int waves, const DecodeArgs& a,
                               hipStream_t stream) {
-  const void* k = pick_kernel(kv_dtype, a.g, flat);
+  const void* k = pick_kernel(kv_dtype, a.g, flat, a.k_new != nullptr);
   void* args[] = {const_cast<DecodeArgs*>(&a)};
   if (flat) {
     return hipLaunchKernel(k, dim3(waves), dim3(64), args, sizeof(int32_t) * (a.B + 1), stream);

@@ -76,6 +76,33 @@ struct Raw<DT_FP8> {
   float scale;  // the block's scale for this KV head, loaded with the block
 };
 
+// One lane's part of one stored row (8 dims of one token), as loaded.
+template <int KV>
+struct RawWord;
+template <>
+struct RawWord<DT_BF16> {
+  using type = u32x4;
+};
+template <>
+struct RawWord<DT_FP8> {
+  using type = u32x2;
+};
+
+// The new token of a decode step whose append is fused into the attention
+// launch (bf16 caches): its K and V rows, this lane's 8 dims (loaded when
+// the wave starts the sequence), and where they go.  blk is the block's
+// index within the sequence (-1: none in this wave); the lanes with
+// q == slot % 4 hold that slot in load slot / 4.  When the walk reaches the
+// block, those lanes store the row into the cache (the append) and put it
+// into the loaded tile in place of the slot's old contents.
+struct NewRow {
+  int blk;
+  int slot;
+  u32x4 k, v;
+  u32x4* k_dst;  // this lane's 16 bytes of the slot in the K and V pools
+  u32x4* v_dst;
+};
+
 // A decode step streams the cache: each tile is read once, so the loads
 // carry the non-temporal hint (NT) and do not displace other data from the
 // L2 and last-level caches (measured: +10-12% gather bandwidth on MI355X).
@@ -303,7 +330,8 @@ __device__ __forceinline__ void softmax_pv_pair(const Half<NG>& a, const Half<NG
 }
 
 // Blocks [jb, je) of KV head h of one request (table row `row`, cached
-// positions < n) folded into `acc`.  Column (lane c of group G) sees the
+// positions < n) folded into `acc`; with FUSED, `nr` is the new row to
+// append and substitute into its block after the load.  Column (lane c of group G) sees the
 // positions <= pcol[G]; p_first (uniform) is the smallest of them.  Decode
 // passes n - 1 for all.  Table entries are read 64 at a time, one per lane.
 // Within each group of up to 64 blocks, loads run DEPTH blocks ahead of the
@@ -314,11 +342,12 @@ __device__ __forceinline__ void softmax_pv_pair(const Half<NG>& a, const Half<NG
 // loads in flight -- and every wait count -- is then the same on every path.
 // DEPTH + 1 is even, so steps come in pairs: the even step keeps its
 // scores and V operands, the odd step completes the pair's softmax and PV.
-template <int KV, int NG, int DEPTH, bool NT = true>
+template <int KV, int NG, int DEPTH, bool NT = true, bool FUSED = false>
 __device__ __forceinline__ void run_blocks(const DecodeArgs& a, const LaneMap& L, u32x4* lds_k,
                                            const bf16x8 (&qop)[NG][4], Acc<NG>& acc,
                                            const int32_t* row, int n, int h, int jb, int je,
-                                           int p_first, const int (&pcol)[NG]) {
+                                           int p_first, const int (&pcol)[NG],
+                                           const NewRow* nr = nullptr) {
   constexpr int kElem = (KV == DT_BF16) ? 2 : 1;
   const size_t head_bytes = static_cast<size_t>(kBS) * kD * kElem;
   const size_t blk_bytes = head_bytes * a.H_KV;
@@ -360,6 +389,22 @@ __device__ __forceinline__ void run_blocks(const DecodeArgs& a, const LaneMap& L
         int lim[NG];
 #pragma unroll
         for (int G = 0; G < NG; ++G) lim[G] = min(pcol[G] - t0, valid - 1);
+        if constexpr (FUSED) {
+          static_assert(KV == DT_BF16, "the fused append stores bf16 rows as they come");
+          if (g0 + i == nr->blk) {  // uniform: the block that holds the new row
+            if (L.q4 == (nr->slot & 3)) {
+              *nr->k_dst = nr->k;
+              *nr->v_dst = nr->v;
+#pragma unroll
+              for (int s = 0; s < 4; ++s) {
+                if (s == (nr->slot >> 2)) {
+                  kbuf[u].w[s] = nr->k;
+                  vbuf[u].w[s] = nr->v;
+                }
+              }
+            }
+          }
+        }
         // even steps keep their scores; odd steps complete the pair
         qk_block<KV, NG>(a.scale_log2, L, lds_k, qop, kbuf[u], vbuf[u], valid, full, lim,
                          half[u & 1]);

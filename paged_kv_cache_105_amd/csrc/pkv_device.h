@@ -156,6 +156,10 @@ struct DecodeArgs {
   // the number of query rows
   const int32_t* query_start;
   int32_t total_q;
+  // decode step with the append fused in: [B][H_KV][d_h] new K and V in the
+  // query dtype, nullptr when the caller appended them already
+  const void* k_new;
+  const void* v_new;
 };
 
 // Request of query row r: the last b with query_start[b] <= r (binary

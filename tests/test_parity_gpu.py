@@ -145,6 +145,50 @@ def test_kv_append_vector_and_element_paths(name, kw, offset):
     _append_only(w, offset)
 
 
+def _fused_step(w, variant, partition_tokens=0):
+    g = lambda t: t.to(DEV).contiguous()
+    kc, vc = g(w.k_cache[0]), g(w.v_cache[0])
+    bt, cl = g(w.block_table), g(w.context_lens)
+    ks = g(w.k_scale[0]) if w.k_scale else None
+    vs = g(w.v_scale[0]) if w.v_scale else None
+    out = torch.full((w.B, w.H_Q, w.d_h), float("nan"), dtype=torch.float32, device=DEV)
+    prev = pkv.set_decode_variant(variant)
+    try:
+        _, _, ws = pkv.decode_plan(w.B, w.H_Q, w.H_KV, w.d_h, w.block_size, w.max_context_len,
+                                   partition_tokens, pkv.dtype_code(w.q[0]),
+                                   pkv.dtype_code(w.k_cache[0]))
+        work = torch.empty(max(ws, 256), dtype=torch.uint8, device=DEV)
+        pkv.decode_step(g(w.k_new[0]), g(w.v_new[0]), out, g(w.q[0]), kc, vc, bt, cl,
+                        w.max_context_len, w.softmax_scale, ks, vs,
+                        partition_tokens=partition_tokens, workspace=work)
+    finally:
+        pkv.set_decode_variant(prev)
+    torch.cuda.synchronize()
+    return kc.cpu(), vc.cpu(), out.cpu().numpy().astype(np.float64)
+
+
+@pytest.mark.parametrize("variant", VARIANTS, ids=VIDS)
+@pytest.mark.parametrize("name,kw", [
+    ("llama8b", dict(lens_after=[1, 16, 17, 31, 32, 33, 600, 2049], H_Q=32, H_KV=8)),
+    ("fp8_gqa", dict(lens_after=[1, 16, 17, 400, 1025, 3000])),
+    ("fp8_mqa", dict(lens_after=[1, 17, 400, 1025])),
+    ("llama8b", dict(lens_after=[5, 300, 40000], H_Q=32, H_KV=8)),
+], ids=lambda x: str(x)[:30])
+def test_decode_step_fused_append(variant, name, kw):
+    """pkv_decode_step (the append inside the attention launch where the MFMA
+    kernels run): pools bit-exact against the oracle's append, outputs within
+    tolerance, and bitwise equal to the separate append + attention calls."""
+    w = make_workload(name, **kw)
+    _log(f"decode_step {name} {kw} variant={variant}")
+    kc, vc, out = _fused_step(w, variant)
+    d = _np(w)
+    rk, rv, ref = oracle_step(w, d)
+    assert np.array_equal(as_numpy(kc), rk) and np.array_equal(as_numpy(vc), rv)
+    assert _err(out, ref) <= TOL
+    _, _, sep = gpu_step(w, variant=variant)
+    assert np.array_equal(out, sep)
+
+
 def test_fp8_append_exhaustive_bf16_inputs():
     # every bf16 bit pattern (NaN and inf included) x 4 scales through the
     # append kernel; codes must equal the oracle's RNE + saturation encoder
