@@ -391,6 +391,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-blocks", type=int, default=0, metavar="N",
                     help="also time pkv_copy_blocks on N random disjoint block pairs")
+    ap.add_argument("--no-cascade", action="store_true",
+                    help="plain decode steps even where requests share prefix blocks")
     ap.add_argument("--no-swap", action="store_true",
                     help="skip the swap-to-host measurement")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -431,6 +433,14 @@ def main():
     pt, parts, ws_bytes = pkv.decode_plan(w.B, w.H_Q, w.H_KV, w.d_h, w.block_size,
                                           w.max_context_len, args.partition,
                                           pkv.dtype_code(w.q[0]), pkv.dtype_code(w.k_cache[0]))
+    # requests that share prefix blocks: the cascade step reads them once
+    cascade = w.shared_blocks > 0 and not args.no_cascade and args.variant in (0, 2)
+    if cascade:
+        splits, cws = pkv.cascade_plan(w.B, w.H_Q, w.H_KV, w.d_h, w.block_size,
+                                       w.max_context_len, w.shared_blocks,
+                                       pkv.dtype_code(w.q[0]), pkv.dtype_code(w.k_cache[0]))
+        ws_bytes = max(ws_bytes, cws)
+        log(f"cascade over {w.shared_blocks} shared blocks, {splits} prefix splits")
     work = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
     out = torch.empty((w.B, w.H_Q, w.d_h), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream()
@@ -442,9 +452,15 @@ def main():
         # launch where the MFMA kernels apply
         for L in range(w.layers):
             kc, vc = pools[r][L]
-            pkv.decode_step(w.k_new[L], w.v_new[L], out, w.q[L], kc, vc, w.block_table,
-                            w.context_lens, w.max_context_len, w.softmax_scale, ks[L], vs[L],
-                            partition_tokens=pt, workspace=work, stream=stream)
+            if cascade:
+                pkv.decode_step_cascade(w.k_new[L], w.v_new[L], out, w.q[L], kc, vc,
+                                        w.block_table, w.context_lens, w.max_context_len,
+                                        w.softmax_scale, w.shared_blocks, ks[L], vs[L],
+                                        workspace=work, stream=stream)
+            else:
+                pkv.decode_step(w.k_new[L], w.v_new[L], out, w.q[L], kc, vc, w.block_table,
+                                w.context_lens, w.max_context_len, w.softmax_scale, ks[L],
+                                vs[L], partition_tokens=pt, workspace=work, stream=stream)
 
     for i in range(args.warmup):
         step(i % R)
@@ -574,6 +590,7 @@ def main():
                    "d_h": w.d_h, "block_size": w.block_size, "kv_dtype": w.kv_dtype,
                    "q_dtype": w.q_dtype, "layers": w.layers, "partition_tokens": pt,
                    "partitions_max": parts, "pool_copies": R,
+                   "cascade_shared_blocks": w.shared_blocks if cascade else 0,
                    "mean_context": round(sum(lens) / len(lens), 1),
                    "us_per_step_per_layer": round(ms_per_step * 1e3 / w.layers, 2),
                    "pct_of_peak_step": round(100 * value / PEAK_GBS, 2),

@@ -311,6 +311,36 @@ int pkv_decode_step(const void* k_new, const void* v_new, float* out, const void
                     float softmax_scale, int32_t partition_tokens, void* workspace,
                     size_t workspace_bytes, pkv_stream_t stream);
 
+/* Cascade decode step over a shared prefix (page 3 "xf_kv_cache",
+ * "End-to-end flow": many requests map the same prefix blocks; page 1
+ * section 21.5 step 3).  Contract: the first shared_blocks entries of every
+ * request's table row are the same physical blocks, every request's
+ * context covers them (context_lens[b] > shared_blocks * block_size, so its
+ * new token lies past the prefix), and shared blocks are not written.  The
+ * result equals pkv_decode_step's up to the order of additions: the shared
+ * blocks are read once per (KV head, 32 query heads of the batch) by a
+ * prefix kernel that scores every request's queries against them, the
+ * flat decode kernel covers each request's private blocks (appending the
+ * new token, fused for bf16 with H_Q / H_KV <= 16, else by the append
+ * kernel first; k_new = v_new = NULL skips the append), and the combine
+ * merges both with the log-sum-exp rule.  Needs the MFMA kernels' shapes
+ * (bf16 queries, bf16 or fp8 cache, d_h 128, 16-slot blocks) and the
+ * balanced split; UNSUPPORTED otherwise (use pkv_decode_step).
+ * pkv_cascade_plan gives the workspace size (and the prefix kernel's split
+ * count); INVALID_ARG if shared_blocks < 1 or the prefix is longer than
+ * max_context_len. */
+int pkv_cascade_plan(int32_t B, int32_t H_Q, int32_t H_KV, int32_t d_h, int32_t block_size,
+                     int32_t max_context_len, int32_t shared_blocks, int q_dtype, int kv_dtype,
+                     int32_t* splits_out, size_t* workspace_bytes);
+int pkv_decode_step_cascade(const void* k_new, const void* v_new, float* out, const void* q,
+                            int q_dtype, void* k_cache, void* v_cache, int kv_dtype,
+                            const float* k_scale, const float* v_scale,
+                            const int32_t* block_table, int32_t max_blocks_per_seq,
+                            const int32_t* context_lens, int32_t max_context_len, int32_t B,
+                            int32_t H_Q, int32_t H_KV, int32_t d_h, int32_t block_size,
+                            int32_t num_blocks, float softmax_scale, int32_t shared_blocks,
+                            void* workspace, size_t workspace_bytes, pkv_stream_t stream);
+
 /* The two launches of pkv_paged_decode_attention, callable separately (for
  * timing each kernel).  decode_partitions runs the online softmax over each
  * piece (same arguments); it writes `out` directly for requests whose

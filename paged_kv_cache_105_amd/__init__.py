@@ -19,6 +19,7 @@ __all__ = ["kv_append", "copy_blocks", "decode_plan", "paged_decode_attention", 
            "combine_partitions", "set_decode_variant", "BlockPool", "PkvError", "load",
            "prefix_root", "block_hashes", "DIGEST_BYTES", "kv_append_chunk",
            "paged_chunk_attention", "swap_record_bytes", "swap_out", "swap_in", "decode_step",
+           "cascade_plan", "decode_step_cascade",
            "PKV_F32", "PKV_BF16", "PKV_FP8_E4M3", "PKV_VARIANT_AUTO", "PKV_VARIANT_GENERIC",
            "PKV_VARIANT_MFMA", "PKV_VARIANT_MFMA_PARTITION", "dtype_code"]
 
@@ -204,6 +205,31 @@ def decode_step(k_new, v_new, out, q, k_cache, v_cache, block_table, context_len
     check(load().pkv_decode_step(_ptr(k_new), _ptr(v_new), *_attn_args(
         out, q, k_cache, v_cache, block_table, context_lens, max_context_len, softmax_scale,
         k_scale, v_scale, partition_tokens, workspace, stream)), "pkv_decode_step")
+
+
+def cascade_plan(B, H_Q, H_KV, d_h, block_size, max_context_len, shared_blocks,
+                 q_dtype=PKV_BF16, kv_dtype=PKV_BF16):
+    """pkv_cascade_plan -> (prefix splits, workspace_bytes)."""
+    sp, ws = C.c_int32(), C.c_size_t()
+    check(load().pkv_cascade_plan(B, H_Q, H_KV, d_h, block_size, max_context_len, shared_blocks,
+                                  q_dtype, kv_dtype, C.byref(sp), C.byref(ws)),
+          "pkv_cascade_plan")
+    return sp.value, ws.value
+
+
+def decode_step_cascade(k_new, v_new, out, q, k_cache, v_cache, block_table, context_lens,
+                        max_context_len, softmax_scale, shared_blocks, k_scale=None,
+                        v_scale=None, workspace=None, stream=None):
+    """pkv_decode_step_cascade: k_new / v_new may be None (no append)."""
+    B, H_Q, d_h = q.shape
+    num_blocks, H_KV, bs, _ = k_cache.shape
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    check(load().pkv_decode_step_cascade(
+        _ptr(k_new), _ptr(v_new), _ptr(out), _ptr(q), _dtype_code(q), _ptr(k_cache),
+        _ptr(v_cache), _dtype_code(k_cache), _ptr(k_scale), _ptr(v_scale), _ptr(block_table),
+        block_table.shape[1], _ptr(context_lens), int(max_context_len), B, H_Q, H_KV, d_h, bs,
+        num_blocks, softmax_scale, int(shared_blocks), _ptr(workspace), ws_bytes,
+        _stream(stream)), "pkv_decode_step_cascade")
 
 
 def decode_partitions(out, q, k_cache, v_cache, block_table, context_lens, max_context_len,

@@ -44,7 +44,8 @@ hipError_t launch_copy_blocks(void* k_cache, void* v_cache, float* k_scale, floa
                               int num_blocks, hipStream_t stream);
 hipError_t launch_combine(float* out, const int32_t* context_lens, const void* ws, int B, int H_Q,
                           int H_KV, int d_h, int partition_tokens, int max_parts,
-                          hipStream_t stream);
+                          int prefix_splits, hipStream_t stream);
+hipError_t launch_prefix_mfma(int kv_dtype, int end_pos, const DecodeArgs& a, hipStream_t stream);
 }  // namespace pkv
 
 namespace {
@@ -463,7 +464,7 @@ int pkv_combine_partitions(float* out, const int32_t* context_lens, int32_t max_
   const int max_parts = (max_context_len + pt - 1) / pt;
   // the workspace header written by the partition call selects the layout
   return hip_status(pkv::launch_combine(out, context_lens, workspace, B, H_Q, H_KV, d_h, pt,
-                                        max_parts, static_cast<hipStream_t>(stream)));
+                                        max_parts, 0, static_cast<hipStream_t>(stream)));
 }
 
 int pkv_paged_decode_attention(float* out, const void* q, int q_dtype, const void* k_cache,
@@ -608,6 +609,128 @@ int pkv_swap_in(void* k_cache, void* v_cache, int kv_dtype, float* k_scale, floa
                 int32_t num_blocks, const void* records, pkv_stream_t stream) {
   return swap_common(false, k_cache, v_cache, kv_dtype, k_scale, v_scale, blocks, n, H_KV, d_h,
                      block_size, num_blocks, records, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+// Split count of a cascade's prefix phase: enough waves to cover the chip
+// about once, at least 8 shared blocks per wave (fewer would make the pieces
+// it writes and the combine reads cost more than the blocks they save), and
+// no empty split.
+int cascade_splits(int B, int g, int H_KV, int shared_blocks) {
+  const long long tiles = (static_cast<long long>(B) * g + 31) / 32 * H_KV;
+  long long want = (1024 + tiles - 1) / tiles;
+  want = std::min<long long>(want, (shared_blocks + 7) / 8);
+  want = std::max<long long>(want, 1);
+  const int bps = static_cast<int>((shared_blocks + want - 1) / want);
+  return (shared_blocks + bps - 1) / bps;
+}
+
+int cascade_plan(int B, int H_Q, int H_KV, int d_h, int block_size, int max_context_len,
+                 int shared_blocks, int q_dtype, int kv_dtype, Plan* plan, int* splits,
+                 size_t* ws) {
+  int st = make_plan(B, H_Q, H_KV, d_h, block_size, max_context_len, 0, q_dtype, kv_dtype, plan);
+  if (st != PKV_OK) return st;
+  if (plan->kernel != K_MFMA_FLAT) return PKV_ERR_UNSUPPORTED;
+  if (shared_blocks < 1 || static_cast<long long>(shared_blocks) * block_size > max_context_len)
+    return PKV_ERR_INVALID_ARG;
+  *splits = cascade_splits(B, H_Q / H_KV, H_KV, shared_blocks);
+  *ws = pkv::cascade_layout(B, H_Q, plan->waves, H_Q / H_KV, d_h, *splits).total;
+  return PKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int pkv_cascade_plan(int32_t B, int32_t H_Q, int32_t H_KV, int32_t d_h, int32_t block_size,
+                     int32_t max_context_len, int32_t shared_blocks, int q_dtype, int kv_dtype,
+                     int32_t* splits_out, size_t* workspace_bytes) {
+  Plan plan;
+  int splits = 0;
+  size_t ws = 0;
+  const int st = cascade_plan(B, H_Q, H_KV, d_h, block_size, max_context_len, shared_blocks,
+                              q_dtype, kv_dtype, &plan, &splits, &ws);
+  if (st != PKV_OK) return st;
+  if (splits_out) *splits_out = splits;
+  if (workspace_bytes) *workspace_bytes = ws;
+  return PKV_OK;
+}
+
+int pkv_decode_step_cascade(const void* k_new, const void* v_new, float* out, const void* q,
+                            int q_dtype, void* k_cache, void* v_cache, int kv_dtype,
+                            const float* k_scale, const float* v_scale,
+                            const int32_t* block_table, int32_t max_blocks_per_seq,
+                            const int32_t* context_lens, int32_t max_context_len, int32_t B,
+                            int32_t H_Q, int32_t H_KV, int32_t d_h, int32_t block_size,
+                            int32_t num_blocks, float softmax_scale, int32_t shared_blocks,
+                            void* workspace, size_t workspace_bytes, pkv_stream_t stream) {
+  int st = check_attention_args(out, q, q_dtype, k_cache, v_cache, kv_dtype, k_scale, v_scale,
+                                block_table, max_blocks_per_seq, context_lens, max_context_len,
+                                B, H_Q, H_KV, d_h, block_size, num_blocks, softmax_scale);
+  if (st != PKV_OK) return st;
+  if (k_new || v_new) {
+    st = check_append_args(k_new, v_new, q_dtype, k_cache, v_cache, kv_dtype, k_scale, v_scale,
+                           block_table, max_blocks_per_seq, context_lens, B, H_KV, d_h,
+                           block_size, num_blocks);
+    if (st != PKV_OK) return st;
+  }
+  Plan plan;
+  int splits = 0;
+  size_t ws = 0;
+  st = cascade_plan(B, H_Q, H_KV, d_h, block_size, max_context_len, shared_blocks, q_dtype,
+                    kv_dtype, &plan, &splits, &ws);
+  if (st != PKV_OK) return st;
+  if (!workspace || workspace_bytes < ws) return PKV_ERR_WORKSPACE;
+  if (reinterpret_cast<uintptr_t>(workspace) & 15) return PKV_ERR_INVALID_ARG;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool fused =
+      k_new && ((reinterpret_cast<uintptr_t>(k_new) | reinterpret_cast<uintptr_t>(v_new)) & 15) == 0 &&
+      pkv::mfma_fuses_append(kv_dtype, H_Q / H_KV);
+  if (k_new && !fused) {
+    st = pkv_kv_append(k_new, v_new, q_dtype, k_cache, v_cache, kv_dtype, k_scale, v_scale,
+                       block_table, max_blocks_per_seq, context_lens, B, H_KV, d_h, block_size,
+                       num_blocks, stream);
+    if (st != PKV_OK) return st;
+  }
+  pkv::DecodeArgs a{};
+  a.out = out;
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
+  a.block_table = block_table;
+  a.context_lens = context_lens;
+  a.ws = static_cast<char*>(workspace);
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.B = B;
+  a.H_Q = H_Q;
+  a.H_KV = H_KV;
+  a.g = H_Q / H_KV;
+  a.d_h = d_h;
+  a.block_size = block_size;
+  a.num_blocks = num_blocks;
+  a.partition_tokens = plan.partition_tokens;
+  a.max_parts = plan.max_parts;
+  a.scale_log2 = softmax_scale * pkv::kLog2e;
+  a.cascade = 1;
+  a.shared_blocks = shared_blocks;
+  a.prefix_splits = splits;
+  a.waves_for_layout = plan.waves;
+  const int end_pos = std::min(shared_blocks * block_size, max_context_len);
+  hipError_t e = pkv::launch_prefix_mfma(kv_dtype, end_pos, a, s);
+  if (e != hipSuccess) return hip_status(e);
+  if (fused) {
+    a.k_new = k_new;
+    a.v_new = v_new;
+  }
+  e = pkv::launch_decode_mfma(kv_dtype, true, plan.waves, a, s);
+  if (e != hipSuccess) return hip_status(e);
+  return hip_status(pkv::launch_combine(out, context_lens, workspace, B, H_Q, H_KV, d_h,
+                                        plan.partition_tokens, plan.max_parts, splits, s));
 }
 
 }  // extern "C"

@@ -11,7 +11,11 @@
 //
 // One wave per (query head, request).  The workspace header says which
 // layout the partition kernel wrote (see pkv_device.h).  Requests whose
-// result the partition kernel wrote directly are skipped.
+// result the partition kernel wrote directly are skipped.  In a cascade
+// over a shared prefix (prefix_splits > 0, flat layout only) every request
+// has pieces: the flat kernel's over its private blocks (or one piece when
+// no wave cut its sequence) and the prefix kernel's prefix_splits pieces
+// over the shared blocks, all merged by the same rule.
 //
 // The kernel is latency bound (a few KiB per wave), so it is organised to
 // keep the number of dependent memory round trips small: each lane loads
@@ -58,7 +62,7 @@ __global__ __launch_bounds__(64) void combine_kernel(float* __restrict__ out,
                                                      const int32_t* __restrict__ context_lens,
                                                      const char* __restrict__ ws, int H_Q,
                                                      int H_KV, int d_h, int partition_tokens,
-                                                     int max_parts) {
+                                                     int max_parts, int prefix_splits) {
   using Vec = typename VecT<VW>::type;
   __shared__ Vec red_s[64 * R];
   const int hq = blockIdx.x, b = blockIdx.y, B = gridDim.y, lane = threadIdx.x;
@@ -66,12 +70,16 @@ __global__ __launch_bounds__(64) void combine_kernel(float* __restrict__ out,
   float* dst = out + (static_cast<size_t>(b) * H_Q + hq) * d_h;
 
   // Locate the pieces: piece k (k < P) has its (m, l) at ml + k * ml_step
-  // and its o at o + k * o_step, piece 0 shifted by (ml_first, o_first).
-  int P = 0;
+  // and its o at o + k * o_step, piece 0 shifted by (ml_first, o_first);
+  // a cascade's prefix pieces k = P .. P + P2 - 1 follow at ml2, o2.
+  int P = 0, P2 = 0;
   const float* ml = nullptr;
   const float* o = nullptr;
+  const float* ml2 = nullptr;
+  const float* o2 = nullptr;
   size_t ml_step = 2, o_step = d_h;  // partition layout: pieces are contiguous
   size_t ml_first = 0, o_first = 0;
+  size_t ml2_step = 0, o2_step = 0;
   if (hd.mode == kWsPartition) {
     const int n = context_lens[b];
     P = min((n + partition_tokens - 1) / partition_tokens, max_parts);
@@ -87,27 +95,56 @@ __global__ __launch_bounds__(64) void combine_kernel(float* __restrict__ out,
     const int h = hq / g, j = hq % g;
     const FlatLayout FL = flat_layout(B, W, g, d_h);
     const int32_t* prefix = reinterpret_cast<const int32_t*>(ws + FL.prefix);
-    const int nb = prefix[b + 1] - prefix[b];
-    if (nb <= 0) return;
-    const long long T = static_cast<long long>(H_KV) * prefix[B];
-    const long long S = static_cast<long long>(H_KV) * prefix[b] + static_cast<long long>(h) * nb;
-    const int first_wave = flat_wave_of(S, T, C);
-    const int last_wave = flat_wave_of(S + nb - 1, T, C);
-    if (first_wave == last_wave) return;  // written final by its wave
-    const int first_slot = flat_chunk_lo(first_wave, T, C) == S ? 0 : 1;
-    P = last_wave - first_wave + 1;
-    const size_t base = (static_cast<size_t>(first_wave) * 2) * g + j;
-    ml = reinterpret_cast<const float*>(ws + FL.ml) + 2 * base;
-    o = reinterpret_cast<const float*>(ws + FL.o) + base * d_h;
-    ml_step = 2 * 2 * static_cast<size_t>(g);
-    o_step = 2 * static_cast<size_t>(g) * d_h;
-    ml_first = 2 * static_cast<size_t>(first_slot) * g;
-    o_first = static_cast<size_t>(first_slot) * g * d_h;
+    const int nb = prefix[b + 1] - prefix[b];  // (a cascade: private blocks only)
+    const size_t rowi = static_cast<size_t>(b) * H_Q + hq;
+    if (prefix_splits > 0) {
+      if (context_lens[b] < 1) return;
+      const CascadeLayout CL = cascade_layout(B, H_Q, W, g, d_h, prefix_splits);
+      const size_t rows = static_cast<size_t>(B) * H_Q;
+      P2 = prefix_splits;
+      ml2 = reinterpret_cast<const float*>(ws + CL.pre_ml) + 2 * rowi;
+      o2 = reinterpret_cast<const float*>(ws + CL.pre_o) + rowi * d_h;
+      ml2_step = 2 * rows;
+      o2_step = rows * d_h;
+      // the private part: one piece for an uncut sequence (below), else as
+      // in the plain layout
+      ml = reinterpret_cast<const float*>(ws + CL.seq_ml) + 2 * rowi;
+      o = reinterpret_cast<const float*>(ws + CL.seq_o) + rowi * d_h;
+      P = nb > 0 ? 1 : 0;
+    } else if (nb <= 0) {
+      return;
+    }
+    if (nb > 0) {
+      const long long T = static_cast<long long>(H_KV) * prefix[B];
+      const long long S =
+          static_cast<long long>(H_KV) * prefix[b] + static_cast<long long>(h) * nb;
+      const int first_wave = flat_wave_of(S, T, C);
+      const int last_wave = flat_wave_of(S + nb - 1, T, C);
+      if (first_wave == last_wave) {
+        if (prefix_splits == 0) return;  // written final by its wave
+      } else {
+        const int first_slot = flat_chunk_lo(first_wave, T, C) == S ? 0 : 1;
+        P = last_wave - first_wave + 1;
+        const size_t base = (static_cast<size_t>(first_wave) * 2) * g + j;
+        ml = reinterpret_cast<const float*>(ws + FL.ml) + 2 * base;
+        o = reinterpret_cast<const float*>(ws + FL.o) + base * d_h;
+        ml_step = 2 * 2 * static_cast<size_t>(g);
+        o_step = 2 * static_cast<size_t>(g) * d_h;
+        ml_first = 2 * static_cast<size_t>(first_slot) * g;
+        o_first = static_cast<size_t>(first_slot) * g * d_h;
+      }
+    }
   } else {
     return;
   }
-  auto ml_at = [&](int k) { return ml + k * ml_step + (k == 0 ? ml_first : 0); };
-  auto o_at = [&](int k) { return o + k * o_step + (k == 0 ? o_first : 0); };
+  const int P1 = P;
+  auto ml_at = [=](int k) {
+    return k < P1 ? ml + k * ml_step + (k == 0 ? ml_first : 0) : ml2 + (k - P1) * ml2_step;
+  };
+  auto o_at = [=](int k) {
+    return k < P1 ? o + k * o_step + (k == 0 ? o_first : 0) : o2 + (k - P1) * o2_step;
+  };
+  P += P2;
 
   // pass 1: every lane merges the pieces lane, lane + 64, ... into its own
   // (m, l); the first chunk's m stays in a register for pass 2
@@ -188,12 +225,12 @@ __global__ __launch_bounds__(64) void combine_kernel(float* __restrict__ out,
 
 hipError_t launch_combine(float* out, const int32_t* context_lens, const void* ws, int B, int H_Q,
                           int H_KV, int d_h, int partition_tokens, int max_parts,
-                          hipStream_t stream) {
+                          int prefix_splits, hipStream_t stream) {
   const dim3 grid(H_Q, B), block(64);
   const char* w = static_cast<const char*>(ws);
 #define PKV_COMBINE(VW, R)                                                                    \
   hipLaunchKernelGGL((combine_kernel<VW, R>), grid, block, 0, stream, out, context_lens, w, H_Q, \
-                     H_KV, d_h, partition_tokens, max_parts)
+                     H_KV, d_h, partition_tokens, max_parts, prefix_splits)
   if (d_h % 4 == 0) {
     PKV_COMBINE(4, 1);  // d_h <= 256: at most 64 columns of 4
   } else if (d_h <= 64) {

@@ -171,13 +171,15 @@ __global__ __launch_bounds__(64, 2) void decode_mfma_flat_kernel(DecodeArgs a) {
   const int B = a.B, HKV = a.H_KV;
   const int cap = a.max_blocks_per_seq;
 
-  // block prefix over requests (n clamped to the table row; n < 1 -> 0 blocks)
+  // block prefix over requests (n clamped to the table row; n < 1 -> 0
+  // blocks); a cascade's phase B counts only the blocks after the shared ones
+  const int skip = a.cascade ? a.shared_blocks : 0;
   int carry = 0;
   for (int b0 = 0; b0 < B; b0 += 64) {
     const int b = b0 + L.lane;
     int nb = 0;
     if (b < B) nb = min(max(a.context_lens[b], 0), cap * kBS);
-    nb = (nb + kBS - 1) / kBS;
+    nb = max((nb + kBS - 1) / kBS - skip, 0);
     int x = nb;  // inclusive scan across the wave
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
@@ -241,14 +243,18 @@ __global__ __launch_bounds__(64, 2) void decode_mfma_flat_kernel(DecodeArgs a) {
     int pcol[NG];
 #pragma unroll
     for (int G = 0; G < NG; ++G) pcol[G] = n - 1;
+    const int jb = static_cast<int>(cur - S) + skip, je = static_cast<int>(pe - S) + skip;
     NewRow nr;
-    if constexpr (FUSED)
-      nr = load_new_row(a, L, b, h, row, static_cast<int>(cur - S), static_cast<int>(pe - S));
-    run_blocks<KV, NG, DEPTH, true, FUSED>(a, L, lds_k, qop, acc, row, n, h,
-                                           static_cast<int>(cur - S), static_cast<int>(pe - S),
-                                           n - 1, pcol, &nr);
+    if constexpr (FUSED) nr = load_new_row(a, L, b, h, row, jb, je);
+    run_blocks<KV, NG, DEPTH, true, FUSED>(a, L, lds_k, qop, acc, row, n, h, jb, je, n - 1, pcol,
+                                           &nr);
     const size_t hq0 = static_cast<size_t>(b) * a.H_Q + static_cast<size_t>(h) * a.g;
-    if (S >= lo && E <= hi) {
+    if (S >= lo && E <= hi && a.cascade) {
+      // whole sequence of a cascade: a piece, merged with the prefix pieces
+      const CascadeLayout CL = cascade_layout(B, a.H_Q, W, a.g, kD, a.prefix_splits);
+      write_state<NG>(acc, L, a.g, nullptr, reinterpret_cast<float*>(a.ws + CL.seq_o) + hq0 * kD,
+                      kD, reinterpret_cast<float*>(a.ws + CL.seq_ml) + hq0 * 2, 2);
+    } else if (S >= lo && E <= hi) {
       write_state<NG>(acc, L, a.g, a.out + hq0 * kD, nullptr, 0, nullptr, 0);
     } else {
       const size_t base = (static_cast<size_t>(w) * 2 + slot) * a.g;

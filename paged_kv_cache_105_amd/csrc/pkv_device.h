@@ -128,6 +128,31 @@ __host__ __device__ inline FlatLayout flat_layout(int B, int W, int g, int d_h) 
   return L;
 }
 
+// Cascade over a shared prefix (the first `shared` blocks of every request's
+// table are the same blocks): after the flat layout, which phase B (the
+// private blocks) uses as usual,
+//   seq_ml[B*H_Q][2], seq_o[B*H_Q][d_h]   phase B's pieces of the (request,
+//                                          head) sequences no wave cut
+//   pre_ml[S][B*H_Q][2], pre_o[S][B*H_Q][d_h]
+//                                          phase A's pieces: split s of the
+//                                          shared blocks, every query head
+// all unnormalised (m, l, o) in log2 units like the other pieces.
+struct CascadeLayout {
+  size_t seq_ml, seq_o, pre_ml, pre_o, total;
+};
+__host__ __device__ inline CascadeLayout cascade_layout(int B, int H_Q, int W, int g, int d_h,
+                                                        int S) {
+  const FlatLayout F = flat_layout(B, W, g, d_h);
+  const size_t rows = static_cast<size_t>(B) * H_Q;
+  CascadeLayout C;
+  C.seq_ml = F.total;
+  C.seq_o = C.seq_ml + ws_align(sizeof(float) * rows * 2);
+  C.pre_ml = C.seq_o + ws_align(sizeof(float) * rows * d_h);
+  C.pre_o = C.pre_ml + ws_align(sizeof(float) * S * rows * 2);
+  C.total = C.pre_o + ws_align(sizeof(float) * S * rows * d_h);
+  return C;
+}
+
 // The chunk [floor(w T / C), floor((w + 1) T / C)) holding block x (C <= T,
 // so no chunk is empty).
 __host__ __device__ inline int flat_wave_of(long long x, long long T, int W) {
@@ -160,6 +185,13 @@ struct DecodeArgs {
   // query dtype, nullptr when the caller appended them already
   const void* k_new;
   const void* v_new;
+  // cascade over a shared prefix: the number of shared leading blocks
+  // (phase B skips them, phase A reads only them) and phase A's split count;
+  // cascade == 0 for a plain decode
+  int32_t cascade;
+  int32_t shared_blocks;
+  int32_t prefix_splits;
+  int32_t waves_for_layout;  // W of the flat layout the cascade regions follow
 };
 
 // Request of query row r: the last b with query_start[b] <= r (binary

@@ -1,0 +1,123 @@
+"""GPU parity of the cascade decode step over a shared prefix
+(pkv_decode_step_cascade) against the float64 oracle.
+
+Page 3 "xf_kv_cache", "End-to-end flow": requests share a 1,200-token
+prefix (75 blocks) and each has private blocks after it.  The cascade reads
+the shared blocks once for all requests and merges the pieces; the result
+must match the oracle's plain decode step (append, then attention over every
+position) within 2e-3, with the pools bit-exact, for bf16 and fp8 caches,
+group sizes 1..32, fewer shared blocks than are actually shared, private
+parts of one block, and the full-size batch (sampled).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import paged_kv_cache_105_amd as pkv
+from oracle import paged
+from paged_kv_cache_105_amd.workloads import as_numpy, make_workload
+
+pytestmark = pytest.mark.gpu
+TOL = 2e-3
+DEV = torch.device("cuda:0")
+
+
+def _np(w):
+    d = dict(q=as_numpy(w.q[0]), k_new=as_numpy(w.k_new[0]), v_new=as_numpy(w.v_new[0]),
+             k_cache=as_numpy(w.k_cache[0]).copy(), v_cache=as_numpy(w.v_cache[0]).copy(),
+             table=as_numpy(w.block_table), lens=as_numpy(w.context_lens))
+    if w.kv_dtype == "fp8_e4m3":
+        d["ks"], d["vs"] = as_numpy(w.k_scale[0]), as_numpy(w.v_scale[0])
+    return d
+
+
+def cascade_step(w, shared_blocks, append=True):
+    g = lambda t: t.to(DEV).contiguous()
+    kc, vc = g(w.k_cache[0]), g(w.v_cache[0])
+    bt, cl = g(w.block_table), g(w.context_lens)
+    ks = g(w.k_scale[0]) if w.k_scale else None
+    vs = g(w.v_scale[0]) if w.v_scale else None
+    _, ws = pkv.cascade_plan(w.B, w.H_Q, w.H_KV, w.d_h, w.block_size, w.max_context_len,
+                             shared_blocks, pkv.dtype_code(w.q[0]), pkv.dtype_code(w.k_cache[0]))
+    work = torch.empty(ws, dtype=torch.uint8, device=DEV)
+    out = torch.full((w.B, w.H_Q, w.d_h), float("nan"), dtype=torch.float32, device=DEV)
+    kn = g(w.k_new[0]) if append else None
+    vn = g(w.v_new[0]) if append else None
+    pkv.decode_step_cascade(kn, vn, out, g(w.q[0]), kc, vc, bt, cl, w.max_context_len,
+                            w.softmax_scale, shared_blocks, ks, vs, workspace=work)
+    torch.cuda.synchronize()
+    return kc.cpu(), vc.cpu(), out.cpu().numpy().astype(np.float64)
+
+
+def oracle_step(w, d, requests=None):
+    return paged.decode_step(d["q"], w.q_dtype, d["k_new"], d["v_new"], d["k_cache"],
+                             d["v_cache"], w.kv_dtype, d["table"], d["lens"], w.block_size,
+                             w.softmax_scale, d.get("ks"), d.get("vs"), requests=requests,
+                             inplace=True)
+
+
+@pytest.mark.parametrize("kw,shared", [
+    (dict(B=6), 75),
+    (dict(B=6), 30),                                        # fewer than actually shared
+    (dict(B=5, kv_dtype="fp8_e4m3"), 75),
+    (dict(B=4, H_Q=8, H_KV=8), 75),                         # g = 1
+    (dict(B=3, H_Q=32, H_KV=1), 75),                        # g = 32
+    (dict(B=7, shared_tokens=64, private_tokens=1, offset_hi=40), 4),   # short private parts
+], ids=lambda x: str(x)[:40])
+def test_cascade_step_matches_oracle(kw, shared):
+    w = make_workload("shared_prefix", layers=1, **kw)
+    print(f"cascade {kw} shared={shared}", flush=True)
+    assert w.shared_blocks >= shared
+    kc, vc, out = cascade_step(w, shared)
+    d = _np(w)
+    rk, rv, ref = oracle_step(w, d)
+    assert np.array_equal(as_numpy(kc), rk) and np.array_equal(as_numpy(vc), rv)
+    assert np.all(np.isfinite(out))
+    assert float(np.max(np.abs(out - ref))) <= TOL
+
+
+def test_cascade_without_append_matches_plain_attention():
+    w = make_workload("shared_prefix", layers=1, B=8)
+    _, _, out = cascade_step(w, 75, append=False)
+    d = _np(w)
+    ref = paged.attend(d["q"], w.q_dtype, d["k_cache"], d["v_cache"], w.kv_dtype, d["table"],
+                       d["lens"], w.block_size, w.softmax_scale)
+    assert float(np.max(np.abs(out - ref))) <= TOL
+
+
+def test_cascade_agrees_with_plain_step():
+    w = make_workload("shared_prefix", layers=1, B=16)
+    _, _, cas = cascade_step(w, 75)
+    g = lambda t: t.to(DEV).contiguous()
+    kc, vc = g(w.k_cache[0]), g(w.v_cache[0])
+    bt, cl = g(w.block_table), g(w.context_lens)
+    _, _, ws = pkv.decode_plan(w.B, w.H_Q, w.H_KV, w.d_h, w.block_size, w.max_context_len)
+    work = torch.empty(max(ws, 256), dtype=torch.uint8, device=DEV)
+    out = torch.empty((w.B, w.H_Q, w.d_h), dtype=torch.float32, device=DEV)
+    pkv.decode_step(g(w.k_new[0]), g(w.v_new[0]), out, g(w.q[0]), kc, vc, bt, cl,
+                    w.max_context_len, w.softmax_scale, workspace=work)
+    torch.cuda.synchronize()
+    assert float(np.max(np.abs(cas - out.cpu().numpy()))) <= 1e-4
+
+
+def test_cascade_full_size_sampled():
+    w = make_workload("shared_prefix", layers=1, device=DEV)
+    assert w.B == 64 and w.shared_blocks == 75
+    _, _, out = cascade_step(w, 75)
+    d = _np(w)
+    req = [0, 31, 63]
+    _, _, ref = oracle_step(w, d, requests=req)
+    assert np.all(np.isfinite(out))
+    assert float(np.max(np.abs(out[req] - ref[req]))) <= TOL
+
+
+def test_cascade_rejects_bad_shapes():
+    w = make_workload("tiny")                   # fp32, d_h 8: no MFMA kernel
+    with pytest.raises(pkv.PkvError) as e:
+        pkv.cascade_plan(w.B, w.H_Q, w.H_KV, w.d_h, w.block_size, w.max_context_len, 1,
+                         pkv.PKV_F32, pkv.PKV_F32)
+    assert e.value.name == "unsupported"
+    with pytest.raises(pkv.PkvError) as e:
+        pkv.cascade_plan(4, 32, 8, 128, 16, 100, 7)   # prefix longer than the contexts
+    assert e.value.name == "invalid_arg"
