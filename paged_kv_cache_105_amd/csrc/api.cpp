@@ -36,7 +36,7 @@ hipError_t launch_decode_generic(int q_dtype, int kv_dtype, const DecodeArgs& a,
 size_t generic_lds_bytes(int g, int d_h, int partition_tokens);
 bool mfma_supports(int q_dtype, int kv_dtype, int d_h, int block_size, int g);
 bool mfma_fuses_append(int kv_dtype, int g);
-int mfma_flat_waves(int kv_dtype, int g, int B);
+int mfma_flat_waves(int kv_dtype, int g, int B, bool cascade);
 hipError_t launch_decode_mfma(int kv_dtype, bool flat, int waves, const DecodeArgs& a,
                               hipStream_t stream);
 hipError_t launch_copy_blocks(void* k_cache, void* v_cache, float* k_scale, float* v_scale,
@@ -45,7 +45,6 @@ hipError_t launch_copy_blocks(void* k_cache, void* v_cache, float* k_scale, floa
 hipError_t launch_combine(float* out, const int32_t* context_lens, const void* ws, int B, int H_Q,
                           int H_KV, int d_h, int partition_tokens, int max_parts,
                           int prefix_splits, hipStream_t stream);
-hipError_t launch_prefix_mfma(int kv_dtype, int end_pos, const DecodeArgs& a, hipStream_t stream);
 }  // namespace pkv
 
 namespace {
@@ -92,7 +91,7 @@ struct Plan {
   size_t total;   // workspace bytes (0: none needed)
 };
 
-int flat_waves_cached(int kv_dtype, int g, int B) {
+int flat_waves_cached(int kv_dtype, int g, int B, bool cascade = false) {
   // the occupancy query depends on the kernel instance and its LDS size
   static std::mutex mu;
   static std::map<std::tuple<int, int, int, int>, int> cache;
@@ -101,11 +100,11 @@ int flat_waves_cached(int kv_dtype, int g, int B) {
     (void)hipGetLastError();
     dev = -1;
   }
-  const auto key = std::make_tuple(dev, kv_dtype, g > 16 ? 2 : 1, B);
+  const auto key = std::make_tuple(dev, kv_dtype, (g > 16 ? 2 : 1) + (cascade ? 4 : 0), B);
   std::lock_guard<std::mutex> lock(mu);
   auto it = cache.find(key);
   if (it != cache.end()) return it->second;
-  int w = pkv::mfma_flat_waves(kv_dtype, g, B);
+  int w = pkv::mfma_flat_waves(kv_dtype, g, B, cascade);
   // PKV_FLAT_WAVES overrides the grid size of the balanced split, for tuning
   // measurements (more waves than fit at once only adds a second round)
   if (const char* e = std::getenv("PKV_FLAT_WAVES")) {
@@ -615,14 +614,18 @@ int pkv_swap_in(void* k_cache, void* v_cache, int kv_dtype, float* k_scale, floa
 
 namespace {
 
-// Split count of a cascade's prefix phase: enough waves to cover the chip
-// about once, at least 8 shared blocks per wave (fewer would make the pieces
-// it writes and the combine reads cost more than the blocks they save), and
-// no empty split.
+// Split count of a cascade's prefix work: enough waves to cover the chip
+// about once, but at least kMinPrefixBlocks shared blocks per wave -- the
+// prefix waves run beside the longer private-block waves of the same
+// launch, so longer splits cost little, while every split adds a piece per
+// (request, head) that is written and read back by the combine -- and no
+// empty split.
+constexpr int kMinPrefixBlocks = 24;
+
 int cascade_splits(int B, int g, int H_KV, int shared_blocks) {
   const long long tiles = (static_cast<long long>(B) * g + 31) / 32 * H_KV;
   long long want = (1024 + tiles - 1) / tiles;
-  want = std::min<long long>(want, (shared_blocks + 7) / 8);
+  want = std::min<long long>(want, (shared_blocks + kMinPrefixBlocks - 1) / kMinPrefixBlocks);
   want = std::max<long long>(want, 1);
   const int bps = static_cast<int>((shared_blocks + want - 1) / want);
   return (shared_blocks + bps - 1) / bps;
@@ -636,6 +639,9 @@ int cascade_plan(int B, int H_Q, int H_KV, int d_h, int block_size, int max_cont
   if (plan->kernel != K_MFMA_FLAT) return PKV_ERR_UNSUPPORTED;
   if (shared_blocks < 1 || static_cast<long long>(shared_blocks) * block_size > max_context_len)
     return PKV_ERR_INVALID_ARG;
+  // the cascade launches the flat kernel's cascade variant: size its grid
+  // (and the layout) by that kernel's occupancy
+  plan->waves = flat_waves_cached(kv_dtype, H_Q / H_KV, B, true);
   *splits = cascade_splits(B, H_Q / H_KV, H_KV, shared_blocks);
   *ws = pkv::cascade_layout(B, H_Q, plan->waves, H_Q / H_KV, d_h, *splits).total;
   return PKV_OK;
@@ -720,14 +726,13 @@ int pkv_decode_step_cascade(const void* k_new, const void* v_new, float* out, co
   a.shared_blocks = shared_blocks;
   a.prefix_splits = splits;
   a.waves_for_layout = plan.waves;
-  const int end_pos = std::min(shared_blocks * block_size, max_context_len);
-  hipError_t e = pkv::launch_prefix_mfma(kv_dtype, end_pos, a, s);
-  if (e != hipSuccess) return hip_status(e);
+  a.prefix_end = std::min(shared_blocks * block_size, max_context_len);
+  a.prefix_waves = splits * H_KV * static_cast<int>((static_cast<long long>(B) * (H_Q / H_KV) + 31) / 32);
   if (fused) {
     a.k_new = k_new;
     a.v_new = v_new;
   }
-  e = pkv::launch_decode_mfma(kv_dtype, true, plan.waves, a, s);
+  hipError_t e = pkv::launch_decode_mfma(kv_dtype, true, plan.waves, a, s);
   if (e != hipSuccess) return hip_status(e);
   return hip_status(pkv::launch_combine(out, context_lens, workspace, B, H_Q, H_KV, d_h,
                                         plan.partition_tokens, plan.max_parts, splits, s));

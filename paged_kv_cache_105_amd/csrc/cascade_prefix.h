@@ -1,6 +1,6 @@
-// Cascade decode over a shared prefix, phase A: the blocks every request of
-// the batch shares are read once per (KV head, column tile) for all of the
-// batch's query heads, instead of once per request.
+// Cascade decode over a shared prefix, the prefix part: the blocks every
+// request of the batch shares are read once per (KV head, column tile) for
+// all of the batch's query heads, instead of once per request.
 //
 // Page 3 "xf_kv_cache", "End-to-end flow" and page 1 "KV cache: Generation
 // state, latency, and allocation", section 21.5 step 3: requests that share
@@ -8,29 +8,34 @@
 // those blocks are the same for all of them, so their scores against each
 // request's query can be computed from one read of each block.  The
 // softmax over a request's positions is then assembled from pieces with the
-// log-sum-exp rule (section 21.1's normalisation, split by position): phase
-// A's pieces over the shared blocks, phase B's (the flat decode kernel run
-// over the private blocks only) over the rest, merged by the combine.
+// log-sum-exp rule (section 21.1's normalisation, split by position): these
+// pieces over the shared blocks, the flat decode kernel's over the rest,
+// merged by the combine.
 //
-// One wave per (split of the shared blocks, tile of 32 columns, KV head); a
-// column is one (request, query head of the group) pair, request-major.  A
-// column's positions end at min(n_r, shared positions) - 1.  Each wave
+// The flat decode kernel runs this on its first prefix_waves workgroups
+// (the others walk the private blocks), so the short prefix waves share the
+// chip with the memory-bound ones instead of taking a launch of their own.
+// Work item id -> (split of the shared blocks, tile of 32 columns, KV head);
+// a column is one (request, query head of the group) pair, request-major.
+// A column's positions end at min(n_r, shared positions) - 1.  Each item
 // writes one unnormalised (m, l, o) piece per column into the cascade's
 // prefix region.
+
+#pragma once
 
 #include "mfma_tiles.h"
 
 namespace pkv {
 
 template <int KV>
-__global__ __launch_bounds__(64, 2) void prefix_mfma_kernel(DecodeArgs a, int end_pos) {
+__device__ __forceinline__ void prefix_wave(const DecodeArgs& a, const LaneMap& L,
+                                            u32x4* lds_k, int id) {
   constexpr int NG = 2;
-  __shared__ u32x4 lds_k[kBS * 16];
-  const LaneMap L = lane_map();
-  const int split = blockIdx.x, tile = blockIdx.y, h = blockIdx.z;
+  const int S = a.prefix_splits;
+  const int split = id % S, h = (id / S) % a.H_KV, tile = id / S / a.H_KV;
   const int g = a.g, cols = a.B * g, c0 = tile * 16 * NG;
   if (c0 >= cols) return;
-  const int SB = a.shared_blocks, S = a.prefix_splits;
+  const int SB = a.shared_blocks, end_pos = a.prefix_end;
   const int bps = (SB + S - 1) / S;
   const int jb = split * bps, je = min(SB, jb + bps);
   const int cap_pos = a.max_blocks_per_seq * kBS;
@@ -89,17 +94,6 @@ __global__ __launch_bounds__(64, 2) void prefix_mfma_kernel(DecodeArgs a, int en
       *reinterpret_cast<f32x4*>(dst + 32 * L.q4 + 8 * ii + 4) = w1;
     }
   }
-}
-
-hipError_t launch_prefix_mfma(int kv_dtype, int end_pos, const DecodeArgs& a,
-                              hipStream_t stream) {
-  const long long cols = static_cast<long long>(a.B) * a.g;
-  const dim3 grid(a.prefix_splits, static_cast<unsigned>((cols + 31) / 32), a.H_KV);
-  if (kv_dtype == DT_BF16)
-    hipLaunchKernelGGL((prefix_mfma_kernel<DT_BF16>), grid, dim3(64), 0, stream, a, end_pos);
-  else
-    hipLaunchKernelGGL((prefix_mfma_kernel<DT_FP8>), grid, dim3(64), 0, stream, a, end_pos);
-  return hipGetLastError();
 }
 
 }  // namespace pkv

@@ -15,6 +15,7 @@
 // step, its operand layouts and its masking are in mfma_tiles.h; a decode
 // column is a query head, and every column sees all n positions.
 
+#include "cascade_prefix.h"
 #include "mfma_tiles.h"
 
 namespace pkv {
@@ -162,12 +163,22 @@ __global__ __launch_bounds__(64, 2) void decode_mfma_kernel(DecodeArgs a) {
 // sequences it overlaps: a sequence inside the chunk is written final, a cut
 // one as a partial in slot 0 (the chunk's first sequence) or slot 1 (its
 // last).
-template <int KV, int NG, int DEPTH, bool FUSED>
+template <int KV, int NG, int DEPTH, bool FUSED, bool CASCADE>
 __global__ __launch_bounds__(64, 2) void decode_mfma_flat_kernel(DecodeArgs a) {
   __shared__ u32x4 lds_k[kBS * 16];
   extern __shared__ int32_t prefix[];  // [B + 1]
   const LaneMap L = lane_map();
-  const int w = blockIdx.x, W = gridDim.x;
+  int w = blockIdx.x, W = gridDim.x;
+  if constexpr (CASCADE) {
+    // the first prefix_waves workgroups score the whole batch against the
+    // shared blocks; the rest walk the private blocks
+    if (w < a.prefix_waves) {
+      prefix_wave<KV>(a, L, lds_k, w);
+      return;
+    }
+    w -= a.prefix_waves;
+    W -= a.prefix_waves;
+  }
   const int B = a.B, HKV = a.H_KV;
   const int cap = a.max_blocks_per_seq;
 
@@ -291,20 +302,23 @@ namespace {
 constexpr int kDepth = 1;
 
 template <int KV, int NG, bool FUSED = false>
-const void* mfma_kernel_ptr(bool flat) {
-  return flat ? reinterpret_cast<const void*>(&decode_mfma_flat_kernel<KV, NG, kDepth, FUSED>)
-              : reinterpret_cast<const void*>(&decode_mfma_kernel<KV, NG, kDepth, FUSED>);
+const void* mfma_kernel_ptr(bool flat, bool cascade) {
+  if (!flat) return reinterpret_cast<const void*>(&decode_mfma_kernel<KV, NG, kDepth, FUSED>);
+  return cascade
+             ? reinterpret_cast<const void*>(&decode_mfma_flat_kernel<KV, NG, kDepth, FUSED, true>)
+             : reinterpret_cast<const void*>(&decode_mfma_flat_kernel<KV, NG, kDepth, FUSED, false>);
 }
 
 // fused: the append runs inside the launch (bf16 caches, one head group;
-// see mfma_fuses_append)
-const void* pick_kernel(int kv_dtype, int g, bool flat, bool fused) {
+// see mfma_fuses_append); cascade: the flat grid also does the prefix work
+const void* pick_kernel(int kv_dtype, int g, bool flat, bool fused, bool cascade) {
   const bool two = g > 16;
   if (kv_dtype == DT_BF16) {
-    if (fused && !two) return mfma_kernel_ptr<DT_BF16, 1, true>(flat);
-    return two ? mfma_kernel_ptr<DT_BF16, 2>(flat) : mfma_kernel_ptr<DT_BF16, 1>(flat);
+    if (fused && !two) return mfma_kernel_ptr<DT_BF16, 1, true>(flat, cascade);
+    return two ? mfma_kernel_ptr<DT_BF16, 2>(flat, cascade)
+               : mfma_kernel_ptr<DT_BF16, 1>(flat, cascade);
   }
-  return two ? mfma_kernel_ptr<DT_FP8, 2>(flat) : mfma_kernel_ptr<DT_FP8, 1>(flat);
+  return two ? mfma_kernel_ptr<DT_FP8, 2>(flat, cascade) : mfma_kernel_ptr<DT_FP8, 1>(flat, cascade);
 }
 }  // namespace
 
@@ -315,8 +329,9 @@ const void* pick_kernel(int kv_dtype, int g, bool flat, bool fused) {
 // for the same matrix and softmax work, so they need every resident wave to
 // keep the memory busy.  (Measured on MI355X: bf16 W = 1024 vs 3072 is
 // 58 vs 65 us on the 8B-style batch; fp8 is best at full occupancy.)
-int mfma_flat_waves(int kv_dtype, int g, int B) {
-  const void* k = pick_kernel(kv_dtype, g, true, false);
+int mfma_flat_waves(int kv_dtype, int g, int B, bool cascade) {
+  const void* k = pick_kernel(kv_dtype, g, true, cascade && mfma_fuses_append(kv_dtype, g),
+                              cascade);
   int dev = 0, cus = 0, per_cu = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
@@ -333,10 +348,12 @@ int mfma_flat_waves(int kv_dtype, int g, int B) {
 
 hipError_t launch_decode_mfma(int kv_dtype, bool flat, int waves, const DecodeArgs& a,
                               hipStream_t stream) {
-  const void* k = pick_kernel(kv_dtype, a.g, flat, a.k_new != nullptr);
+  const bool cascade = a.cascade != 0;
+  const void* k = pick_kernel(kv_dtype, a.g, flat, a.k_new != nullptr, cascade);
   void* args[] = {const_cast<DecodeArgs*>(&a)};
   if (flat) {
-    return hipLaunchKernel(k, dim3(waves), dim3(64), args, sizeof(int32_t) * (a.B + 1), stream);
+    const int grid = waves + (cascade ? a.prefix_waves : 0);
+    return hipLaunchKernel(k, dim3(grid), dim3(64), args, sizeof(int32_t) * (a.B + 1), stream);
   }
   return hipLaunchKernel(k, dim3(a.max_parts, a.H_KV, a.B), dim3(64), args, 0, stream);
 }

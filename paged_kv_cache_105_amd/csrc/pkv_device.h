@@ -192,6 +192,8 @@ struct DecodeArgs {
   int32_t shared_blocks;
   int32_t prefix_splits;
   int32_t waves_for_layout;  // W of the flat layout the cascade regions follow
+  int32_t prefix_waves;      // leading workgroups of the flat grid that do prefix work
+  int32_t prefix_end;        // positions the prefix work reads: min(shared, max context)
 };
 
 // Request of query row r: the last b with query_start[b] <= r (binary
