@@ -163,7 +163,101 @@ __global__ __launch_bounds__(64, 2) void decode_mfma_kernel(DecodeArgs a) {
 // sequences it overlaps: a sequence inside the chunk is written final, a cut
 // one as a partial in slot 0 (the chunk's first sequence) or slot 1 (its
 // last).
-template <int KV, int NG, int DEPTH, bool FUSED, bool CASCADE>
+//
+// The walk is one stream of loads over the whole chunk.  It moves in groups
+// of up to 64 blocks of one sequence (one table entry per lane); when a group
+// starts, the next group's table entries (and, for a new sequence, its
+// length) are requested, and the last step of a group already loads the next
+// group's first block, so neither a table window nor a change of sequence
+// lets the loads run dry.
+
+typedef const __attribute__((address_space(4))) int32_t* const_i32p;
+
+// The fused append, split for the streaming walk: where the new row goes
+// (from the request's raw length and one table entry, both read through the
+// scalar cache) and, issued separately and early, the row's K and V.  The
+// rules are those of load_new_row: nothing is appended for a length or block
+// id out of range, or when the wave's blocks [jb, je) miss the row's block.
+__device__ __forceinline__ void new_row_place(const DecodeArgs& a, const LaneMap& L,
+                                              const_i32p table, int b, int h, int n_raw,
+                                              int jb, int je, NewRow& nr) {
+  nr.blk = -1;
+  nr.slot = 0;
+  if (n_raw < 1 || n_raw > a.max_blocks_per_seq * kBS) return;
+  const int jn = (n_raw - 1) / kBS;
+  if (jn < jb || jn >= je) return;
+  const int p = table[static_cast<size_t>(b) * a.max_blocks_per_seq + jn];
+  if (p < 0 || p >= a.num_blocks) return;
+  nr.blk = jn;
+  nr.slot = (n_raw - 1) % kBS;
+  const size_t dst = ((static_cast<size_t>(p) * a.H_KV + h) * kBS + nr.slot) * kD + 8 * L.c;
+  nr.k_dst = reinterpret_cast<u32x4*>(static_cast<uint16_t*>(const_cast<void*>(a.k_cache)) + dst);
+  nr.v_dst = reinterpret_cast<u32x4*>(static_cast<uint16_t*>(const_cast<void*>(a.v_cache)) + dst);
+}
+__device__ __forceinline__ void new_row_load(const DecodeArgs& a, const LaneMap& L, int b, int h,
+                                             NewRow& nr) {
+  const size_t src = (static_cast<size_t>(b) * a.H_KV + h) * kD + 8 * L.c;
+  nr.k = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.k_new) + src);
+  nr.v = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.v_new) + src);
+}
+
+// Where the walk is: sequence (b, h) with nb blocks (after any skipped
+// shared ones) starting at flat index S, and the group of nblk <= 64 of its
+// blocks starting at flat index x; nblk == 0 past the end of the chunk.
+// Every field is the same in all lanes.
+struct Cursor {
+  long long S, x;
+  int b, h, nb, nblk;
+};
+
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// The group after c inside [.., hi): the next blocks of the same sequence,
+// else the first group of the next sequence that has blocks.
+__device__ __forceinline__ Cursor next_group(Cursor c, long long hi, const int32_t* prefix,
+                                             int B, int HKV) {
+  const long long E = c.S + c.nb;
+  const long long seg_end = E < hi ? E : hi;
+  const long long nx = c.x + c.nblk;
+  if (nx < seg_end) {
+    c.x = nx;
+    c.nblk = static_cast<int>(seg_end - nx < 64 ? seg_end - nx : 64);
+    return c;
+  }
+  if (E >= hi) {
+    c.nblk = 0;
+    return c;
+  }
+  if (++c.h == HKV) {
+    c.h = 0;
+    do {
+      ++c.b;
+    } while (c.b < B && prefix[c.b + 1] == prefix[c.b]);
+    if (c.b >= B) {  // cannot happen while E < hi <= T; keeps prefix[] in bounds
+      c.nblk = 0;
+      return c;
+    }
+    c.nb = uniform(prefix[c.b + 1] - prefix[c.b]);
+  }
+  c.S = E;
+  c.x = E;
+  const long long e2 = E + c.nb < hi ? E + c.nb : hi;
+  c.nblk = static_cast<int>(e2 - E < 64 ? e2 - E : 64);
+  return c;
+}
+
+// Table entries of a group, one per lane (lanes past the group read nothing);
+// ids are clamped where they are used, so nothing waits for them here.
+__device__ __forceinline__ int load_window(const DecodeArgs& a, const Cursor& c, int skip,
+                                           int lane) {
+  int v = 0;
+  if (lane < c.nblk)
+    v = a.block_table[static_cast<size_t>(c.b) * a.max_blocks_per_seq +
+                      static_cast<int>(c.x - c.S) + skip + lane];
+  return v;
+}
+
+template <int KV, int NG, bool FUSED, bool CASCADE>
 __global__ __launch_bounds__(64, 2) void decode_mfma_flat_kernel(DecodeArgs a) {
   __shared__ u32x4 lds_k[kBS * 16];
   extern __shared__ int32_t prefix[];  // [B + 1]
@@ -202,7 +296,7 @@ __global__ __launch_bounds__(64, 2) void decode_mfma_flat_kernel(DecodeArgs a) {
   }
   if (L.lane == 0) prefix[0] = 0;
   lds_wave_sync();
-  const long long T = static_cast<long long>(HKV) * prefix[B];
+  const long long T = static_cast<long long>(HKV) * uniform(prefix[B]);
   // chunks of at least one block each: with more waves than blocks the
   // surplus waves stay idle (an empty chunk would leave a hole in the
   // sequence of pieces the combine walks)
@@ -224,64 +318,183 @@ __global__ __launch_bounds__(64, 2) void decode_mfma_flat_kernel(DecodeArgs a) {
   const long long lo = flat_chunk_lo(w, T, C);
   const long long hi = flat_chunk_lo(w + 1, T, C);
 
-  // request holding block lo: the last b with H_KV * P_b <= lo
-  int b = 0;
+  // the sequence holding block lo: request = the last b with H_KV * P_b <= lo
+  Cursor cur;
   {
     int l0 = 0, l1 = B - 1;
     while (l0 < l1) {
       const int mid = (l0 + l1 + 1) >> 1;
       if (static_cast<long long>(HKV) * prefix[mid] <= lo) l0 = mid; else l1 = mid - 1;
     }
-    b = l0;
+    cur.b = uniform(l0);
+    const int pb = uniform(prefix[cur.b]);
+    cur.nb = uniform(prefix[cur.b + 1]) - pb;
+    cur.h = static_cast<int>((lo - static_cast<long long>(HKV) * pb) / cur.nb);
+    cur.S = static_cast<long long>(HKV) * pb + static_cast<long long>(cur.h) * cur.nb;
+    cur.x = lo;
+    const long long e = cur.S + cur.nb < hi ? cur.S + cur.nb : hi;
+    cur.nblk = static_cast<int>(e - lo < 64 ? e - lo : 64);
   }
-  int nb = prefix[b + 1] - prefix[b];
-  int h = static_cast<int>((lo - static_cast<long long>(HKV) * prefix[b]) / nb);
   float* part_o = reinterpret_cast<float*>(a.ws + FL.o);
   float* part_ml = reinterpret_cast<float*>(a.ws + FL.ml);
 
-  long long cur = lo;
+  constexpr int kElem = (KV == DT_BF16) ? 2 : 1;
+  const size_t head_bytes = static_cast<size_t>(kBS) * kD * kElem;
+  Raw<KV> kbuf[2], vbuf[2];
+  // load block id p (clamped into the pool) of KV head hh
+  auto issue = [&](Raw<KV>& kr, Raw<KV>& vr, int p, int hh) {
+    p = min(max(p, 0), a.num_blocks - 1);
+    const size_t off = (static_cast<size_t>(p) * HKV + hh) * head_bytes;
+    load_raw<KV, true>(kr, static_cast<const char*>(a.k_cache) + off, L.lane);
+    load_raw<KV, true>(vr, static_cast<const char*>(a.v_cache) + off, L.lane);
+    if constexpr (KV == DT_FP8) {
+      kr.scale = a.k_scale[static_cast<size_t>(p) * HKV + hh];
+      vr.scale = a.v_scale[static_cast<size_t>(p) * HKV + hh];
+    }
+    // keep the scheduler from sinking these loads below the block being
+    // processed (that would shrink the distance they run ahead)
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  // context lengths and the first two table entries of each group are read
+  // through the scalar cache (uniform indices; neither changes during the
+  // launch), so their waits never hold up the vector loads of the stream
+  const_i32p lens = (const_i32p)(a.context_lens);
+  const_i32p table = (const_i32p)(a.block_table);
+  auto seg_bounds = [&](const Cursor& c, int& jb, int& je) {
+    const long long s0 = c.S > lo ? c.S : lo;
+    const long long s1 = c.S + c.nb < hi ? c.S + c.nb : hi;
+    jb = static_cast<int>(s0 - c.S) + skip;
+    je = static_cast<int>(s1 - c.S) + skip;
+  };
+  int win0 = load_window(a, cur, skip, L.lane);
+  const int n_raw0 = lens[cur.b];
+  int n0 = min(n_raw0, cap * kBS);
+  bf16x8 qop[NG][4];
+  load_q<NG>(a, L, cur.b, cur.h, qop);
+  NewRow nr;
+  if constexpr (FUSED) {
+    int jb, je;
+    seg_bounds(cur, jb, je);
+    new_row_place(a, L, table, cur.b, cur.h, n_raw0, jb, je, nr);
+    new_row_load(a, L, cur.b, cur.h, nr);
+  }
+  issue(kbuf[0], vbuf[0], __builtin_amdgcn_readlane(win0, 0), cur.h);
+  issue(kbuf[1], vbuf[1], __builtin_amdgcn_readlane(win0, min(1, cur.nblk - 1)), cur.h);
+  Acc<NG> acc;
+  acc_init<NG>(acc);
   int slot = 0;
-  while (cur < hi) {
-    const long long S = static_cast<long long>(HKV) * prefix[b] + static_cast<long long>(h) * nb;
-    const long long E = S + nb;
-    const long long pe = E < hi ? E : hi;
-    const int n = min(a.context_lens[b], a.max_blocks_per_seq * kBS);
-    bf16x8 qop[NG][4];
-    load_q<NG>(a, L, b, h, qop);
-    Acc<NG> acc;
-    acc_init<NG>(acc);
-    const int32_t* row = a.block_table + static_cast<size_t>(b) * a.max_blocks_per_seq;
-    int pcol[NG];
+
+  // One group: blocks [c.x, c.x + c.nblk) of sequence (c.b, c.h) with n
+  // cached positions and table entries `win`; the loads of its first two
+  // steps are already on the way.  Each step processes its block and then
+  // loads the block two steps ahead: a later block of this group (the last
+  // one again for a padding step), or one of the next group's first two.
+  // Requests the next group's table entries into win_nxt and its sequence
+  // length into n_nxt, and returns that group in nxt (nblk == 0: the chunk
+  // is done).  The walk calls it with two window registers in turn, so a
+  // window still on its way is never copied (a copy would wait for every
+  // load in flight).
+  auto group = [&](const Cursor& c, int n, int win, Cursor& nxt, int& win_nxt, int& n_nxt) {
+    nxt = next_group(c, hi, prefix, B, HKV);
+    const bool more = nxt.nblk > 0;
+    const bool new_seq = more && nxt.x == nxt.S;
+    win_nxt = load_window(a, nxt, skip, L.lane);
+    int p_nxt0 = 0, p_nxt1 = 0;
+    if (more) {
+      const size_t e = static_cast<size_t>(nxt.b) * cap + static_cast<int>(nxt.x - nxt.S) + skip;
+      p_nxt0 = table[e];
+      p_nxt1 = nxt.nblk > 1 ? table[e + 1] : p_nxt0;
+    }
+    const int n_raw_nxt = new_seq ? lens[nxt.b] : n;
+    n_nxt = min(n_raw_nxt, cap * kBS);
+    const int jb = static_cast<int>(c.x - c.S) + skip;
+    __builtin_assume(c.nblk >= 1);  // a group has at least one block
+    const int nsteps = (c.nblk + 1) & ~1;
+    int lim[NG];
+    Half<NG> half[2];
+    int i0 = 0;
+    do {
 #pragma unroll
-    for (int G = 0; G < NG; ++G) pcol[G] = n - 1;
-    const int jb = static_cast<int>(cur - S) + skip, je = static_cast<int>(pe - S) + skip;
-    NewRow nr;
-    if constexpr (FUSED) nr = load_new_row(a, L, b, h, row, jb, je);
-    run_blocks<KV, NG, DEPTH, true, FUSED>(a, L, lds_k, qop, acc, row, n, h, jb, je, n - 1, pcol,
-                                           &nr);
-    const size_t hq0 = static_cast<size_t>(b) * a.H_Q + static_cast<size_t>(h) * a.g;
-    if (S >= lo && E <= hi && a.cascade) {
-      // whole sequence of a cascade: a piece, merged with the prefix pieces
-      const CascadeLayout CL = cascade_layout(B, a.H_Q, W, a.g, kD, a.prefix_splits);
-      write_state<NG>(acc, L, a.g, nullptr, reinterpret_cast<float*>(a.ws + CL.seq_o) + hq0 * kD,
-                      kD, reinterpret_cast<float*>(a.ws + CL.seq_ml) + hq0 * 2, 2);
-    } else if (S >= lo && E <= hi) {
-      write_state<NG>(acc, L, a.g, a.out + hq0 * kD, nullptr, 0, nullptr, 0);
-    } else {
-      const size_t base = (static_cast<size_t>(w) * 2 + slot) * a.g;
-      write_state<NG>(acc, L, a.g, nullptr, part_o + base * kD, kD, part_ml + base * 2, 2);
+      for (int u = 0; u < 2; ++u) {
+        const int i = i0 + u;
+        const int t0 = (jb + i) * kBS;
+        const int valid = i < c.nblk ? n - t0 : 0;
+#pragma unroll
+        for (int G = 0; G < NG; ++G) lim[G] = valid - 1;
+        if constexpr (FUSED) {
+          if (jb + i == nr.blk) {  // uniform: the block that holds the new row
+            if (L.q4 == (nr.slot & 3)) {
+              *nr.k_dst = nr.k;
+              *nr.v_dst = nr.v;
+#pragma unroll
+              for (int s = 0; s < 4; ++s) {
+                if (s == (nr.slot >> 2)) {
+                  kbuf[u].w[s] = nr.k;
+                  vbuf[u].w[s] = nr.v;
+                }
+              }
+            }
+          }
+        }
+        // even steps keep their scores; odd steps complete the pair
+        qk_block<KV, NG>(a.scale_log2, L, lds_k, qop, kbuf[u], vbuf[u], valid, valid >= kBS,
+                         lim, half[u]);
+        if (u == 1) softmax_pv_pair<NG>(half[0], half[1], acc);
+        if (u == 1 && i == nsteps - 1 && new_seq) {
+          // the group's last QK is done: the next sequence's Q (and new
+          // row) go out between its first two blocks, so every wait for
+          // them is one the first block needs anyway
+          load_q<NG>(a, L, nxt.b, nxt.h, qop);
+          if constexpr (FUSED) new_row_load(a, L, nxt.b, nxt.h, nr);
+        }
+        // the load of step i + 2, into the buffer this step has used
+        const int j = i + 2;
+        int p, hh = c.h;
+        if (j < nsteps) {
+          p = __builtin_amdgcn_readlane(win, min(j, c.nblk - 1));
+        } else if (more) {
+          p = j == nsteps ? p_nxt0 : p_nxt1;
+          hh = nxt.h;
+        } else {
+          p = __builtin_amdgcn_readlane(win, c.nblk - 1);
+        }
+        issue(kbuf[u], vbuf[u], p, hh);
+      }
+      i0 += 2;
+    } while (i0 < nsteps);
+    if (!more || new_seq) {
+      // the sequence's part in this chunk is done
+      const long long S = c.S, E = c.S + c.nb;
+      const size_t hq0 = static_cast<size_t>(c.b) * a.H_Q + static_cast<size_t>(c.h) * a.g;
+      if (S >= lo && E <= hi && a.cascade) {
+        // whole sequence of a cascade: a piece, merged with the prefix pieces
+        const CascadeLayout CL = cascade_layout(B, a.H_Q, W, a.g, kD, a.prefix_splits);
+        write_state<NG>(acc, L, a.g, nullptr,
+                        reinterpret_cast<float*>(a.ws + CL.seq_o) + hq0 * kD, kD,
+                        reinterpret_cast<float*>(a.ws + CL.seq_ml) + hq0 * 2, 2);
+      } else if (S >= lo && E <= hi) {
+        write_state<NG>(acc, L, a.g, a.out + hq0 * kD, nullptr, 0, nullptr, 0);
+      } else {
+        const size_t base = (static_cast<size_t>(w) * 2 + slot) * a.g;
+        write_state<NG>(acc, L, a.g, nullptr, part_o + base * kD, kD, part_ml + base * 2, 2);
+      }
+      slot = 1;
+      if (new_seq) {
+        acc_init<NG>(acc);
+        if constexpr (FUSED) {
+          int jb2, je2;
+          seg_bounds(nxt, jb2, je2);
+          new_row_place(a, L, table, nxt.b, nxt.h, n_raw_nxt, jb2, je2, nr);
+        }
+      }
     }
-    slot = 1;
-    cur = pe;
-    // next sequence with at least one block
-    if (++h == HKV) {
-      h = 0;
-      do {
-        ++b;
-      } while (b < B && prefix[b + 1] == prefix[b]);
-      if (b >= B) break;
-      nb = prefix[b + 1] - prefix[b];
-    }
+    return more;
+  };
+
+  Cursor cur1;
+  int win1, n1;
+  while (group(cur, n0, win0, cur1, win1, n1) && group(cur1, n1, win1, cur, win0, n0)) {
   }
 }
 
@@ -305,8 +518,8 @@ template <int KV, int NG, bool FUSED = false>
 const void* mfma_kernel_ptr(bool flat, bool cascade) {
   if (!flat) return reinterpret_cast<const void*>(&decode_mfma_kernel<KV, NG, kDepth, FUSED>);
   return cascade
-             ? reinterpret_cast<const void*>(&decode_mfma_flat_kernel<KV, NG, kDepth, FUSED, true>)
-             : reinterpret_cast<const void*>(&decode_mfma_flat_kernel<KV, NG, kDepth, FUSED, false>);
+             ? reinterpret_cast<const void*>(&decode_mfma_flat_kernel<KV, NG, FUSED, true>)
+             : reinterpret_cast<const void*>(&decode_mfma_flat_kernel<KV, NG, FUSED, false>);
 }
 
 // fused: the append runs inside the launch (bf16 caches, one head group;
