@@ -42,9 +42,9 @@ hipError_t launch_decode_mfma(int kv_dtype, bool flat, int waves, const DecodeAr
 hipError_t launch_copy_blocks(void* k_cache, void* v_cache, float* k_scale, float* v_scale,
                               const int32_t* pairs, int n_pairs, size_t block_bytes, int H_KV,
                               int num_blocks, hipStream_t stream);
-hipError_t launch_combine(float* out, const int32_t* context_lens, const void* ws, int B, int H_Q,
-                          int H_KV, int d_h, int partition_tokens, int max_parts,
-                          int prefix_splits, hipStream_t stream);
+hipError_t launch_combine(float* out, const int32_t* context_lens, const void* ws,
+                          size_t ws_bytes, int B, int H_Q, int H_KV, int d_h, int partition_tokens,
+                          int max_parts, int prefix_splits, hipStream_t stream);
 }  // namespace pkv
 
 namespace {
@@ -462,8 +462,9 @@ int pkv_combine_partitions(float* out, const int32_t* context_lens, int32_t max_
   if (pt % block_size) return PKV_ERR_INVALID_ARG;
   const int max_parts = (max_context_len + pt - 1) / pt;
   // the workspace header written by the partition call selects the layout
-  return hip_status(pkv::launch_combine(out, context_lens, workspace, B, H_Q, H_KV, d_h, pt,
-                                        max_parts, 0, static_cast<hipStream_t>(stream)));
+  return hip_status(pkv::launch_combine(out, context_lens, workspace, workspace_bytes, B, H_Q,
+                                        H_KV, d_h, pt, max_parts, 0,
+                                        static_cast<hipStream_t>(stream)));
 }
 
 int pkv_paged_decode_attention(float* out, const void* q, int q_dtype, const void* k_cache,
@@ -734,8 +735,9 @@ int pkv_decode_step_cascade(const void* k_new, const void* v_new, float* out, co
   }
   hipError_t e = pkv::launch_decode_mfma(kv_dtype, true, plan.waves, a, s);
   if (e != hipSuccess) return hip_status(e);
-  return hip_status(pkv::launch_combine(out, context_lens, workspace, B, H_Q, H_KV, d_h,
-                                        plan.partition_tokens, plan.max_parts, splits, s));
+  return hip_status(pkv::launch_combine(out, context_lens, workspace, workspace_bytes, B, H_Q,
+                                        H_KV, d_h, plan.partition_tokens, plan.max_parts, splits,
+                                        s));
 }
 
 }  // extern "C"

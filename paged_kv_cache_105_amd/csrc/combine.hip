@@ -60,14 +60,28 @@ __device__ inline void lse_merge(float& m, float& l, float m2, float l2) {
 template <int VW, int R>
 __global__ __launch_bounds__(64) void combine_kernel(float* __restrict__ out,
                                                      const int32_t* __restrict__ context_lens,
-                                                     const char* __restrict__ ws, int H_Q,
-                                                     int H_KV, int d_h, int partition_tokens,
-                                                     int max_parts, int prefix_splits) {
+                                                     const char* __restrict__ ws,
+                                                     size_t ws_bytes, int H_Q, int H_KV, int d_h,
+                                                     int partition_tokens, int max_parts,
+                                                     int prefix_splits) {
   using Vec = typename VecT<VW>::type;
   __shared__ Vec red_s[64 * R];
   const int hq = blockIdx.x, b = blockIdx.y, B = gridDim.y, lane = threadIdx.x;
-  const WsHeader hd = *reinterpret_cast<const WsHeader*>(ws);
   float* dst = out + (static_cast<size_t>(b) * H_Q + hq) * d_h;
+
+  // One round trip for everything the piece lookup needs: the header, this
+  // request's length and (flat layout) the block prefix, which starts right
+  // after the header; the prefix words are read whenever they lie inside the
+  // workspace, whatever the layout, and used only for the flat one.
+  const WsHeader hd = *reinterpret_cast<const WsHeader*>(ws);
+  const int n_b = context_lens[b];
+  int pre_b = 0, pre_b1 = 0, pre_B = 0;
+  if (kWsHeader + sizeof(int32_t) * (static_cast<size_t>(B) + 1) <= ws_bytes) {
+    const int32_t* pre = reinterpret_cast<const int32_t*>(ws + kWsHeader);
+    pre_b = pre[b];
+    pre_b1 = pre[b + 1];
+    pre_B = pre[B];
+  }
 
   // Locate the pieces: piece k (k < P) has its (m, l) at ml + k * ml_step
   // and its o at o + k * o_step, piece 0 shifted by (ml_first, o_first);
@@ -81,8 +95,7 @@ __global__ __launch_bounds__(64) void combine_kernel(float* __restrict__ out,
   size_t ml_first = 0, o_first = 0;
   size_t ml2_step = 0, o2_step = 0;
   if (hd.mode == kWsPartition) {
-    const int n = context_lens[b];
-    P = min((n + partition_tokens - 1) / partition_tokens, max_parts);
+    P = min((n_b + partition_tokens - 1) / partition_tokens, max_parts);
     if (P <= 1) return;
     const PartitionLayout PL = partition_layout(B, H_Q, max_parts, d_h);
     const size_t base = (static_cast<size_t>(b) * H_Q + hq) * max_parts;
@@ -94,11 +107,10 @@ __global__ __launch_bounds__(64) void combine_kernel(float* __restrict__ out,
     const int W = hd.waves, C = hd.chunks, g = hd.g;
     const int h = hq / g, j = hq % g;
     const FlatLayout FL = flat_layout(B, W, g, d_h);
-    const int32_t* prefix = reinterpret_cast<const int32_t*>(ws + FL.prefix);
-    const int nb = prefix[b + 1] - prefix[b];  // (a cascade: private blocks only)
+    const int nb = pre_b1 - pre_b;  // (a cascade: private blocks only)
     const size_t rowi = static_cast<size_t>(b) * H_Q + hq;
     if (prefix_splits > 0) {
-      if (context_lens[b] < 1) return;
+      if (n_b < 1) return;
       const CascadeLayout CL = cascade_layout(B, H_Q, W, g, d_h, prefix_splits);
       const size_t rows = static_cast<size_t>(B) * H_Q;
       P2 = prefix_splits;
@@ -115,9 +127,8 @@ __global__ __launch_bounds__(64) void combine_kernel(float* __restrict__ out,
       return;
     }
     if (nb > 0) {
-      const long long T = static_cast<long long>(H_KV) * prefix[B];
-      const long long S =
-          static_cast<long long>(H_KV) * prefix[b] + static_cast<long long>(h) * nb;
+      const long long T = static_cast<long long>(H_KV) * pre_B;
+      const long long S = static_cast<long long>(H_KV) * pre_b + static_cast<long long>(h) * nb;
       const int first_wave = flat_wave_of(S, T, C);
       const int last_wave = flat_wave_of(S + nb - 1, T, C);
       if (first_wave == last_wave) {
@@ -146,6 +157,30 @@ __global__ __launch_bounds__(64) void combine_kernel(float* __restrict__ out,
   };
   P += P2;
 
+  // pass 2's lane layout: lanes are split into PPI groups of LP lanes; group
+  // s reads piece i * PPI + s of a chunk of 64 pieces on iteration i, lane c
+  // of a group reads vector columns c, c + 64, ... of that piece's row
+  const int ncol = d_h / VW;
+  const int LP = ncol < 64 ? ncol : 64;
+  const int PPI = 64 / LP;
+  const int sub = lane / LP, c = lane % LP;
+  const bool on = sub < PPI;
+  // the o rows of the first kUnroll iterations go out together with the
+  // (m, l) loads of pass 1 (their addresses do not depend on any weight)
+  const int kn0 = min(64, P);
+  Vec x0[kUnroll][R];
+#pragma unroll
+  for (int u = 0; u < kUnroll; ++u) {
+    const int kk = u * PPI + sub;
+    const bool valid = on && kk < kn0;
+    const Vec* row = reinterpret_cast<const Vec*>(o_at(valid ? kk : 0));
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int col = c + r * 64;
+      x0[u][r] = (valid && col < ncol) ? row[col] : Vec(0.f);
+    }
+  }
+
   // pass 1: every lane merges the pieces lane, lane + 64, ... into its own
   // (m, l); the first chunk's m stays in a register for pass 2
   float m_own = -INFINITY, m_lane = -INFINITY, l_lane = 0.f;
@@ -164,14 +199,8 @@ __global__ __launch_bounds__(64) void combine_kernel(float* __restrict__ out,
   }
   const float M = m_lane, inv = 1.0f / l_lane;
 
-  // pass 2: lanes are split into PPI groups of LP lanes; group s reads piece
-  // i * PPI + s of the chunk on iteration i, lane c of a group reads vector
-  // columns c, c + 64, ... of that piece's row
-  const int ncol = d_h / VW;
-  const int LP = ncol < 64 ? ncol : 64;
-  const int PPI = 64 / LP;
-  const int sub = lane / LP, c = lane % LP;
-  const bool on = sub < PPI;
+  // pass 2: weights 2^(m_k - M) / L, held by lane k of each chunk of 64
+  // pieces and read with a lane shuffle
   Vec acc[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) acc[r] = Vec(0.f);
@@ -188,11 +217,16 @@ __global__ __launch_bounds__(64) void combine_kernel(float* __restrict__ out,
         const int kk = (i0 + u) * PPI + sub;     // piece within the chunk
         const bool valid = on && kk < kn;
         wk[u] = __shfl(w, valid ? kk : 0, 64);
-        const Vec* row = reinterpret_cast<const Vec*>(o_at(k0 + (valid ? kk : 0)));
+        if (k0 == 0 && i0 == 0) {
 #pragma unroll
-        for (int r = 0; r < R; ++r) {
-          const int col = c + r * 64;
-          x[u][r] = (valid && col < ncol) ? row[col] : Vec(0.f);
+          for (int r = 0; r < R; ++r) x[u][r] = x0[u][r];
+        } else {
+          const Vec* row = reinterpret_cast<const Vec*>(o_at(k0 + (valid ? kk : 0)));
+#pragma unroll
+          for (int r = 0; r < R; ++r) {
+            const int col = c + r * 64;
+            x[u][r] = (valid && col < ncol) ? row[col] : Vec(0.f);
+          }
         }
         if (!valid) wk[u] = 0.f;
       }
@@ -223,14 +257,14 @@ __global__ __launch_bounds__(64) void combine_kernel(float* __restrict__ out,
   }
 }
 
-hipError_t launch_combine(float* out, const int32_t* context_lens, const void* ws, int B, int H_Q,
-                          int H_KV, int d_h, int partition_tokens, int max_parts,
-                          int prefix_splits, hipStream_t stream) {
+hipError_t launch_combine(float* out, const int32_t* context_lens, const void* ws,
+                          size_t ws_bytes, int B, int H_Q, int H_KV, int d_h, int partition_tokens,
+                          int max_parts, int prefix_splits, hipStream_t stream) {
   const dim3 grid(H_Q, B), block(64);
   const char* w = static_cast<const char*>(ws);
 #define PKV_COMBINE(VW, R)                                                                    \
-  hipLaunchKernelGGL((combine_kernel<VW, R>), grid, block, 0, stream, out, context_lens, w, H_Q, \
-                     H_KV, d_h, partition_tokens, max_parts, prefix_splits)
+  hipLaunchKernelGGL((combine_kernel<VW, R>), grid, block, 0, stream, out, context_lens, w,        \
+                     ws_bytes, H_Q, H_KV, d_h, partition_tokens, max_parts, prefix_splits)
   if (d_h % 4 == 0) {
     PKV_COMBINE(4, 1);  // d_h <= 256: at most 64 columns of 4
   } else if (d_h <= 64) {

@@ -539,9 +539,13 @@ const void* pick_kernel(int kv_dtype, int g, bool flat, bool fused, bool cascade
 // once.  bf16 blocks (8 KiB of K and V per KV head) stream best with one wave
 // per SIMD -- longer chunks amortise each wave's start (lengths, table, first
 // block) and fewer streams contend for HBM; fp8 blocks carry half the bytes
-// for the same matrix and softmax work, so they need every resident wave to
-// keep the memory busy.  (Measured on MI355X: bf16 W = 1024 vs 3072 is
-// 58 vs 65 us on the 8B-style batch; fp8 is best at full occupancy.)
+// for the same matrix and softmax work, so with one head group they need
+// every resident wave to keep the memory busy.  With two head groups (g > 16)
+// every cut sequence writes 32 heads of partials (16.6 KiB per piece), so
+// fewer, longer chunks win there too.  (Measured on MI355X: bf16 W = 1024 vs
+// 3072 is 58 vs 65 us on the 8B-style batch; fp8 with one group is best at
+// full occupancy; fp8 MQA, W = 512 / 1024 / 1536 / 2048 / 3072: 53.1 / 40.6 /
+// 41.1 / 44.0 / 54.6 us.)
 int mfma_flat_waves(int kv_dtype, int g, int B, bool cascade) {
   const void* k = pick_kernel(kv_dtype, g, true, cascade && mfma_fuses_append(kv_dtype, g),
                               cascade);
@@ -555,7 +559,7 @@ int mfma_flat_waves(int kv_dtype, int g, int B, bool cascade) {
     return 256 * 4;
   }
   const int simds_per_cu = 4;
-  if (kv_dtype == DT_BF16) per_cu = per_cu < simds_per_cu ? per_cu : simds_per_cu;
+  if (kv_dtype == DT_BF16 || g > 16) per_cu = per_cu < simds_per_cu ? per_cu : simds_per_cu;
   return cus * per_cu;
 }
 
