@@ -52,7 +52,11 @@ template <int KV, int NG>
 __global__ __launch_bounds__(64, 2) void chunk_mfma_kernel(DecodeArgs a) {
   __shared__ u32x4 lds_k[kBS * 16];
   const LaneMap L = lane_map();
-  const int tile = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  // one-dimensional grid over (request, KV head, tile), tile fastest, laid
+  // out so that the tiles of a (request, KV head) share an XCD's L2
+  const int item = xcd_block(blockIdx.x, gridDim.x);
+  const int tile = item % a.chunk_tiles;
+  const int h = (item / a.chunk_tiles) % a.H_KV, b = item / a.chunk_tiles / a.H_KV;
   int qs0, n_new, ctx;
   if (!chunk_bounds(a, b, qs0, n_new, ctx)) return;
   const int g = a.g, cols = n_new * g, c0 = tile * 16 * NG;
@@ -201,12 +205,16 @@ constexpr int kChunkNG = 2;  // columns per wave: 16 x kChunkNG
 hipError_t launch_chunk_mfma(int kv_dtype, int max_q_len, const DecodeArgs& a,
                              hipStream_t stream) {
   const long long cols = static_cast<long long>(max_q_len) * a.g;
-  const dim3 grid(static_cast<unsigned>((cols + 16 * kChunkNG - 1) / (16 * kChunkNG)), a.H_KV,
-                  a.B);
+  const long long tiles = (cols + 16 * kChunkNG - 1) / (16 * kChunkNG);
+  const long long items = tiles * a.H_KV * a.B;
+  if (items > 0x7fffffffLL) return hipErrorInvalidValue;
+  DecodeArgs ta = a;
+  ta.chunk_tiles = static_cast<int32_t>(tiles);
+  const dim3 grid(static_cast<unsigned>(items));
   if (kv_dtype == DT_BF16)
-    hipLaunchKernelGGL((chunk_mfma_kernel<DT_BF16, kChunkNG>), grid, dim3(64), 0, stream, a);
+    hipLaunchKernelGGL((chunk_mfma_kernel<DT_BF16, kChunkNG>), grid, dim3(64), 0, stream, ta);
   else
-    hipLaunchKernelGGL((chunk_mfma_kernel<DT_FP8, kChunkNG>), grid, dim3(64), 0, stream, a);
+    hipLaunchKernelGGL((chunk_mfma_kernel<DT_FP8, kChunkNG>), grid, dim3(64), 0, stream, ta);
   return hipGetLastError();
 }
 

@@ -194,7 +194,21 @@ struct DecodeArgs {
   int32_t waves_for_layout;  // W of the flat layout the cascade regions follow
   int32_t prefix_waves;      // leading workgroups of the flat grid that do prefix work
   int32_t prefix_end;        // positions the prefix work reads: min(shared, max context)
+  int32_t chunk_tiles;       // chunk kernel: column tiles per (request, KV head)
 };
+
+// Workgroups are dispatched to the 8 XCDs of the device round robin (id i
+// runs on XCD i mod 8), and each XCD has its own L2.  xcd_block gives
+// workgroup i the logical item that puts a contiguous eighth of the logical
+// order on each XCD, so items that read the same data -- the column tiles of
+// one request and KV head -- share an L2.  Any device is correct with it;
+// only where work lands changes.
+constexpr int kXcds = 8;
+__device__ __forceinline__ int xcd_block(int i, int n) {
+  const int x = i % kXcds, j = i / kXcds;
+  const int q = n / kXcds, r = n % kXcds;
+  return (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + j;
+}
 
 // Request of query row r: the last b with query_start[b] <= r (binary
 // search; query_start is non-decreasing).  Used by the chunk kernels.
