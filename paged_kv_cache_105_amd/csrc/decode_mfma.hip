@@ -280,23 +280,25 @@ __global__ __launch_bounds__(64, 2) void decode_mfma_flat_kernel(DecodeArgs a) {
   // blocks); a cascade's phase B counts only the blocks after the shared ones
   const int skip = a.cascade ? a.shared_blocks : 0;
   int carry = 0;
+  int x = 0;  // lane l ends with prefix[b0 + l + 1] of the last 64 requests
   for (int b0 = 0; b0 < B; b0 += 64) {
     const int b = b0 + L.lane;
     int nb = 0;
     if (b < B) nb = min(max(a.context_lens[b], 0), cap * kBS);
     nb = max((nb + kBS - 1) / kBS - skip, 0);
-    int x = nb;  // inclusive scan across the wave
+    x = nb;  // inclusive scan across the wave
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
       const int y = __shfl_up(x, off, 64);
       if (L.lane >= off) x += y;
     }
-    if (b < B) prefix[b + 1] = carry + x;
-    carry += __shfl(x, 63, 64);
+    x += carry;
+    if (b < B) prefix[b + 1] = x;
+    carry = __builtin_amdgcn_readlane(x, 63);
   }
   if (L.lane == 0) prefix[0] = 0;
   lds_wave_sync();
-  const long long T = static_cast<long long>(HKV) * uniform(prefix[B]);
+  const long long T = static_cast<long long>(HKV) * carry;
   // chunks of at least one block each: with more waves than blocks the
   // surplus waves stay idle (an empty chunk would leave a hole in the
   // sequence of pieces the combine walks)
@@ -315,21 +317,45 @@ __global__ __launch_bounds__(64, 2) void decode_mfma_flat_kernel(DecodeArgs a) {
     for (int i = L.lane; i <= B; i += 64) wp[i] = prefix[i];
   }
   if (w >= C) return;
-  const long long lo = flat_chunk_lo(w, T, C);
-  const long long hi = flat_chunk_lo(w + 1, T, C);
+  // this wave's chunk [floor(w T / C), floor((w + 1) T / C)): in 32 bits
+  // (floor(w T / C) = w floor(T / C) + floor(w (T mod C) / C)) whenever the
+  // operands allow, which avoids the long 64-bit division sequences
+  const bool small = T < (1LL << 31) && C <= 46340;
+  long long lo, hi;
+  if (small) {
+    const int Ti = static_cast<int>(T), q = Ti / C, r = Ti % C;
+    lo = w * q + (w * r) / C;
+    hi = (w + 1) * q + ((w + 1) * r) / C;
+  } else {
+    lo = flat_chunk_lo(w, T, C);
+    hi = flat_chunk_lo(w + 1, T, C);
+  }
 
   // the sequence holding block lo: request = the last b with H_KV * P_b <= lo
   Cursor cur;
   {
-    int l0 = 0, l1 = B - 1;
-    while (l0 < l1) {
-      const int mid = (l0 + l1 + 1) >> 1;
-      if (static_cast<long long>(HKV) * prefix[mid] <= lo) l0 = mid; else l1 = mid - 1;
+    int pb, pb1;
+    if (B <= 64) {
+      // the prefix is still in the lanes (lane l: P_(l+1)): the requests
+      // with H_KV * P_(b) <= lo, b >= 1, are lanes 0 .. count - 1
+      const bool le = L.lane < B && static_cast<long long>(HKV) * x <= lo;
+      const int count = __builtin_popcountll(__ballot(le));
+      cur.b = min(count, B - 1);
+      pb = cur.b == 0 ? 0 : __builtin_amdgcn_readlane(x, cur.b - 1);
+      pb1 = __builtin_amdgcn_readlane(x, cur.b);
+    } else {
+      int l0 = 0, l1 = B - 1;
+      while (l0 < l1) {
+        const int mid = (l0 + l1 + 1) >> 1;
+        if (static_cast<long long>(HKV) * prefix[mid] <= lo) l0 = mid; else l1 = mid - 1;
+      }
+      cur.b = uniform(l0);
+      pb = uniform(prefix[cur.b]);
+      pb1 = uniform(prefix[cur.b + 1]);
     }
-    cur.b = uniform(l0);
-    const int pb = uniform(prefix[cur.b]);
-    cur.nb = uniform(prefix[cur.b + 1]) - pb;
-    cur.h = static_cast<int>((lo - static_cast<long long>(HKV) * pb) / cur.nb);
+    cur.nb = pb1 - pb;
+    cur.h = small ? (static_cast<int>(lo) - HKV * pb) / cur.nb
+                  : static_cast<int>((lo - static_cast<long long>(HKV) * pb) / cur.nb);
     cur.S = static_cast<long long>(HKV) * pb + static_cast<long long>(cur.h) * cur.nb;
     cur.x = lo;
     const long long e = cur.S + cur.nb < hi ? cur.S + cur.nb : hi;
