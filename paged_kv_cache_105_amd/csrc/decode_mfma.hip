@@ -4,16 +4,20 @@
 // Page 1 "KV cache: Generation state, latency, and allocation", section 21.1:
 // the g = H_Q / H_KV query heads of a group read the same KV head but keep
 // separate scores; section 21.5: attention reads each position through the
-// block table.  One wave (one workgroup) per (partition, KV head, request):
-// each K/V block of the KV head is loaded once and used by all g query heads
-// of the group, which makes the per-block work two small dense products:
+// block table.  A wave works on one KV head of one request at a time: each
+// K/V block of the KV head is loaded once and used by all g query heads of
+// the group, which makes the per-block work two small dense products:
 //
-//   S[token][head] = K_blk[16 x 128] . Q^T[128 x 16]      (4 x MFMA 16x16x32)
-//   O^T[dim][head] += V_blk^T[128 x 16] . P^T[16 x 16]    (8 x 2 x MFMA 16x16x16)
+//   S[token][head] = K_blk[16 x 128] . Q^T[128 x 16]       (4 x MFMA 16x16x32)
+//   O^T[dim][head] += V_pair^T[128 x 32] . P^T[32 x 16]    (8 x 2 x MFMA 16x16x32
+//                                                            per pair of blocks)
 //
 // (head groups of 16; g <= 16 uses one group, g = 32 two).  The per-block
 // step, its operand layouts and its masking are in mfma_tiles.h; a decode
-// column is a query head, and every column sees all n positions.
+// column is a query head, and every column sees all n positions.  Two
+// kernels: the partition kernel (one wave per (partition, KV head,
+// request)) and the flat kernel (the balanced split below), which is the
+// one the library picks for batches up to 8192 requests.
 
 #include "cascade_prefix.h"
 #include "mfma_tiles.h"

@@ -327,6 +327,49 @@ def test_run_to_run_bitwise_deterministic():
     assert np.array_equal(a, b)
 
 
+def test_workspace_reuse_across_shapes():
+    # One workspace, first filled with bytes no call wrote, serves calls of
+    # several shapes in turn (other requests, other head counts) and the
+    # same shapes again: every call writes the header and the layout it
+    # uses, so results match the oracle and repeat bit for bit.
+    shapes = [dict(lens_after=[5, 900, 2000, 3000], H_Q=32, H_KV=8),
+              dict(lens_after=[1, 17, 40000], H_Q=8, H_KV=2),
+              dict(lens_after=list(range(1, 129)), H_Q=32, H_KV=8)]
+    work = torch.full((64 << 20,), 0xFF, dtype=torch.uint8, device=DEV)
+    refs = {}
+    for rep in range(2):
+        for i, kw in enumerate(shapes):
+            w = make_workload("llama8b", **kw)
+            g = lambda t: t.to(DEV).contiguous()
+            kc, vc = g(w.k_cache[0]), g(w.v_cache[0])
+            bt, cl = g(w.block_table), g(w.context_lens)
+            _, _, ws = pkv.decode_plan(w.B, w.H_Q, w.H_KV, w.d_h, w.block_size,
+                                       w.max_context_len, 0, pkv.dtype_code(w.q[0]),
+                                       pkv.dtype_code(w.k_cache[0]))
+            assert ws <= work.numel()
+            outs = []
+            for call in range(2):
+                out = torch.full((w.B, w.H_Q, w.d_h), float("nan"), dtype=torch.float32,
+                                 device=DEV)
+                pkv.paged_decode_attention(out, g(w.q[0]), kc, vc, bt, cl, w.max_context_len,
+                                           w.softmax_scale, workspace=work)
+                torch.cuda.synchronize()
+                outs.append(out.cpu().numpy().astype(np.float64))
+            assert np.array_equal(outs[0], outs[1])
+            if i not in refs:
+                req = sorted(set([0, w.B // 2, w.B - 1]))
+                d = _np(w)  # attention only: the cache as it is, no append
+                ref = paged.attend(d["q"], w.q_dtype, d["k_cache"], d["v_cache"], w.kv_dtype,
+                                   d["table"], d["lens"], w.block_size, w.softmax_scale,
+                                   requests=req)
+                e = _err(outs[0], ref, req)
+                _log(f"workspace reuse shape {i} err={e:.2e}")
+                assert e <= TOL
+                refs[i] = outs[0]
+            else:
+                assert np.array_equal(refs[i], outs[0])
+
+
 # ---------------------------------------------------------------------------
 # paging invariants (bitwise)
 # ---------------------------------------------------------------------------
