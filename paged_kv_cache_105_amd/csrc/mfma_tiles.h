@@ -263,6 +263,28 @@ __device__ __forceinline__ void qk_block(float scale_log2, const LaneMap& L, u32
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
+// Maximum without the quieting of signalling NaNs that fmaxf costs on this
+// target (one extra instruction per operand): gfx950's v_maximum3_f32.  A
+// NaN operand gives NaN; the scores it is used on are finite or -inf.
+__device__ __forceinline__ float fmax_fast(float a, float b) {
+  return __builtin_elementwise_maximum(a, b);
+}
+
+// Maximum over the four lanes l, l ^ 16, l ^ 32, l ^ 48 (the quarters of one
+// column), in registers: permlane16_swap exchanges the odd 16-lane rows of
+// its first operand with the even rows of its second, permlane32_swap the
+// upper 32 lanes of the first with the lower 32 of the second, so with both
+// operands equal to x each lane ends up with its partner's value in one of
+// the two results.
+__device__ __forceinline__ float colmax4(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  const float y = fmax_fast(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const uint32_t v = __float_as_uint(y);
+  const auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return fmax_fast(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
 // Online softmax and PV over a pair of blocks (32 positions) with K = 32
 // products: MFMA k-index 8q + i is token q + 4i of block a for i < 4 and
 // token q + 4(i - 4) of block b for i >= 4, so each lane builds both
@@ -283,10 +305,10 @@ __device__ __forceinline__ void softmax_pv_pair(const Half<NG>& a, const Half<NG
   }
 #pragma unroll
   for (int G = 0; G < NG; ++G) {
-    float mx = fmaxf(fmaxf(fmaxf(a.s2[G][0], a.s2[G][1]), fmaxf(a.s2[G][2], a.s2[G][3])),
-                     fmaxf(fmaxf(b.s2[G][0], b.s2[G][1]), fmaxf(b.s2[G][2], b.s2[G][3])));
-    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    float mx = fmax_fast(
+        fmax_fast(fmax_fast(a.s2[G][0], a.s2[G][1]), fmax_fast(a.s2[G][2], a.s2[G][3])),
+        fmax_fast(fmax_fast(b.s2[G][0], b.s2[G][1]), fmax_fast(b.s2[G][2], b.s2[G][3])));
+    mx = colmax4(mx);
     // raise the running max only when needed (uniform branch over the wave;
     // the first real block always takes it since m starts at -inf)
     if (__any(mx > acc.m[G] + kRescaleSlack)) {
