@@ -475,7 +475,7 @@ def test_full_llama8b_all_requests():
 
 
 @pytest.mark.parametrize("name,req", [("long32k", [0, 7]), ("fp8_gqa", [0, 5, 77, 127]),
-                                      ("fp8_mqa", [1, 64, 126])])
+                                      ("fp8_mqa", [1, 64, 126]), ("fp8_mha", [0, 63, 127])])
 def test_full_size_sampled(name, req):
     w = make_workload(name)
     _log(f"{name} full: B={w.B} max_len={w.max_context_len} blocks={w.num_blocks}")
