@@ -280,8 +280,9 @@ int pkv_decode_plan(int32_t B, int32_t H_Q, int32_t H_KV, int32_t d_h, int32_t b
  * values (they may hold anything, NaN included).  `max_context_len` (a host
  * value) must be >= every context_lens[b]; it sizes the grid.  Supported
  * (q_dtype, kv_dtype): (F32, F32), (BF16, BF16), (BF16, FP8_E4M3).
- * q, k_cache, v_cache, out and workspace must be 16-byte aligned
- * (INVALID_ARG otherwise).
+ * softmax_scale must be finite and > 0 (the usual 1 / sqrt(d_h)), and q,
+ * k_cache, v_cache, out and workspace 16-byte aligned (INVALID_ARG
+ * otherwise).
  * `workspace` holds partial results of requests whose positions are split
  * over several waves; its size comes from pkv_decode_plan with the same
  * arguments (WORKSPACE if too small; it may be NULL when the plan says 0).

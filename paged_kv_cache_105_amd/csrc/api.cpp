@@ -178,7 +178,7 @@ int check_attention_args(const float* out, const void* q, int q_dtype, const voi
   if (static_cast<long long>(max_context_len) >
       static_cast<long long>(max_blocks_per_seq) * block_size)
     return PKV_ERR_INVALID_ARG;
-  if (!std::isfinite(softmax_scale)) return PKV_ERR_INVALID_ARG;
+  if (!std::isfinite(softmax_scale) || !(softmax_scale > 0.0f)) return PKV_ERR_INVALID_ARG;
   if (kv_dtype == PKV_FP8_E4M3 && (!k_scale || !v_scale)) return PKV_ERR_INVALID_ARG;
   const bool pair_ok = (q_dtype == PKV_F32 && kv_dtype == PKV_F32) ||
                        (q_dtype == PKV_BF16 && kv_dtype == PKV_BF16) ||

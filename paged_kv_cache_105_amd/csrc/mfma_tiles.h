@@ -205,10 +205,16 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 }
 
 // Scores and V operands of one block, kept until its pair is complete.
+// The score in log2 units is s2 * kscale: bf16 blocks keep the raw product
+// q . k and kscale = softmax_scale * log2(e), which folds the scaling into
+// the exponent's fused multiply-add (and into one product of the block's
+// max), so it needs kscale > 0; fp8 blocks, whose scale can have any sign,
+// are scaled as they come out of the MFMA and carry kscale = 1.
 template <int NG>
 struct Half {
-  float s2[NG][4];  // scores of tokens q + 4i for this lane's column, log2 units
+  float s2[NG][4];  // scores of tokens q + 4i for this lane's column
   u32x4 vb[4];      // V: token 4s + q, dims 8c .. 8c + 7 (bf16 pairs)
+  float kscale;     // log2-unit score = s2 * kscale
   float vscale;     // fp8 V scale of the block (1 for bf16)
 };
 
@@ -232,9 +238,11 @@ __device__ __forceinline__ void qk_block(float scale_log2, const LaneMap& L, u32
   for (int j = 0; j < 4; ++j) ka[j] = __builtin_bit_cast(bf16x8, lds_k[L.rpos[j]]);
 
   float kscale = scale_log2;
+  out.kscale = scale_log2;
   out.vscale = 1.0f;
   if constexpr (KV == DT_FP8) {
     kscale *= kr.scale;
+    out.kscale = 1.0f;
     out.vscale = vr.scale;
   }
   // ---- V operands: token q + 4i, dim 8c + n  (zero the invalid rows)
@@ -252,7 +260,7 @@ __device__ __forceinline__ void qk_block(float scale_log2, const LaneMap& L, u32
     for (int j = 0; j < 4; ++j)
       sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[j], qop[G][j], sc, 0, 0, 0);
 #pragma unroll
-    for (int ii = 0; ii < 4; ++ii) out.s2[G][ii] = sc[ii] * kscale;
+    for (int ii = 0; ii < 4; ++ii) out.s2[G][ii] = (KV == DT_FP8) ? sc[ii] * kscale : sc[ii];
     if (!full) {
 #pragma unroll
       for (int ii = 0; ii < 4; ++ii)
@@ -305,10 +313,11 @@ __device__ __forceinline__ void softmax_pv_pair(const Half<NG>& a, const Half<NG
   }
 #pragma unroll
   for (int G = 0; G < NG; ++G) {
-    float mx = fmax_fast(
-        fmax_fast(fmax_fast(a.s2[G][0], a.s2[G][1]), fmax_fast(a.s2[G][2], a.s2[G][3])),
-        fmax_fast(fmax_fast(b.s2[G][0], b.s2[G][1]), fmax_fast(b.s2[G][2], b.s2[G][3])));
-    mx = colmax4(mx);
+    const float mxa =
+        fmax_fast(fmax_fast(a.s2[G][0], a.s2[G][1]), fmax_fast(a.s2[G][2], a.s2[G][3]));
+    const float mxb =
+        fmax_fast(fmax_fast(b.s2[G][0], b.s2[G][1]), fmax_fast(b.s2[G][2], b.s2[G][3]));
+    const float mx = colmax4(fmax_fast(mxa * a.kscale, mxb * b.kscale));
     // raise the running max only when needed (uniform branch over the wave;
     // the first real block always takes it since m starts at -inf)
     if (__any(mx > acc.m[G] + kRescaleSlack)) {
@@ -322,8 +331,9 @@ __device__ __forceinline__ void softmax_pv_pair(const Half<NG>& a, const Half<NG
     float pr[8];
 #pragma unroll
     for (int ii = 0; ii < 4; ++ii) {
-      pr[ii] = __builtin_amdgcn_exp2f(a.s2[G][ii] - acc.m[G]);       // 0 if masked
-      pr[4 + ii] = __builtin_amdgcn_exp2f(b.s2[G][ii] - acc.m[G]);
+      // 0 if masked
+      pr[ii] = __builtin_amdgcn_exp2f(__builtin_fmaf(a.s2[G][ii], a.kscale, -acc.m[G]));
+      pr[4 + ii] = __builtin_amdgcn_exp2f(__builtin_fmaf(b.s2[G][ii], b.kscale, -acc.m[G]));
     }
     acc.l[G] += ((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7]));
     // probabilities (times the fp8 V scale) as hi + lo bf16 pairs

@@ -525,6 +525,11 @@ def test_invalid_arguments_are_rejected():
     with pytest.raises(pkv.PkvError) as e:
         pkv.paged_decode_attention(out30, q30, kc, vc, bt, cl, w.max_context_len, 0.1)
     assert e.value.name == "invalid_arg"
+    # softmax_scale must be finite and positive
+    for bad in (0.0, -0.1, float("nan"), float("inf")):
+        with pytest.raises(pkv.PkvError) as e:
+            pkv.paged_decode_attention(out, q, kc, vc, bt, cl, w.max_context_len, bad)
+        assert e.value.name == "invalid_arg"
     # partition not a multiple of the block size
     with pytest.raises(pkv.PkvError):
         pkv.decode_plan(2, 32, 8, 128, 16, 2000, 24)
