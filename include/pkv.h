@@ -397,8 +397,8 @@ int pkv_kv_append_chunk(const void* k_new, const void* v_new, int in_dtype, void
  *   out[row][hq][:] = sum_{t <= p} exp(s_t - max s) V_t / sum_{t <= p} exp(s_t - max s),
  *   s_t = softmax_scale * q[row][hq] . K_t,
  * in fp32.  max_q_len (host) >= every n_b sizes the grid; max_context_len
- * (host) >= every context length.  Same dtype pairs and alignment as
- * pkv_paged_decode_attention; B and H_Q at most 65535.  No workspace: the
+ * (host) >= every context length.  Same dtype pairs, alignment and
+ * softmax_scale rule as pkv_paged_decode_attention; B and H_Q at most 65535.  No workspace: the
  * outputs are written directly.  Call after pkv_kv_append_chunk. */
 int pkv_paged_chunk_attention(float* out, const void* q, int q_dtype, const void* k_cache,
                               const void* v_cache, int kv_dtype, const float* k_scale,
