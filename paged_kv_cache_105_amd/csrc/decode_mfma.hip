@@ -470,7 +470,7 @@ __global__ __launch_bounds__(64, 2) void decode_mfma_flat_kernel(DecodeArgs a) {
         // even steps keep their scores; odd steps complete the pair
         qk_block<KV, NG>(a.scale_log2, L, lds_k, qop, kbuf[u], vbuf[u], valid, valid >= kBS,
                          lim, half[u]);
-        if (u == 1) softmax_pv_pair<NG>(half[0], half[1], acc);
+        if (u == 1) softmax_pv_pair<KV, NG>(half[0], half[1], acc);
         if (u == 1 && i == nsteps - 1 && new_seq) {
           // the group's last QK is done: the next sequence's Q (and new
           // row) go out between its first two blocks, so every wait for

@@ -213,7 +213,8 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 template <int NG>
 struct Half {
   float s2[NG][4];  // scores of tokens q + 4i for this lane's column
-  u32x4 vb[4];      // V: token 4s + q, dims 8c .. 8c + 7 (bf16 pairs)
+  u32x4 vb[4];      // V: token 4s + q, dims 8c .. 8c + 7 (bf16 pairs; fp8
+                    // blocks keep the 8 codes in .x, .y)
   float kscale;     // log2-unit score = s2 * kscale
   float vscale;     // fp8 V scale of the block (1 for bf16)
 };
@@ -247,7 +248,14 @@ __device__ __forceinline__ void qk_block(float scale_log2, const LaneMap& L, u32
   }
   // ---- V operands: token q + 4i, dim 8c + n  (zero the invalid rows)
 #pragma unroll
-  for (int s = 0; s < 4; ++s) out.vb[s] = as_bf16x8<KV>(vr, s);
+  for (int s = 0; s < 4; ++s) {
+    if constexpr (KV == DT_BF16) {
+      out.vb[s] = vr.w[s];
+    } else {
+      // the 8 codes, widened with the PV operands
+      out.vb[s] = __builtin_shufflevector(vr.w[s], u32x2{0u, 0u}, 0, 1, 2, 3);
+    }
+  }
   if (valid < kBS) {
 #pragma unroll
     for (int s = 0; s < 4; ++s)
@@ -297,19 +305,53 @@ __device__ __forceinline__ float colmax4(float x) {
 // products: MFMA k-index 8q + i is token q + 4i of block a for i < 4 and
 // token q + 4(i - 4) of block b for i >= 4, so each lane builds both
 // operands from what it holds.
-template <int NG>
+// Two V values of dim 8c + n, tokens 4s + q and 4(s + 1) + q, as a bf16
+// pair (low half: the first token) for n = 2m and n = 2m + 1 from the
+// stored words w0 (token 4s + q) and w1 (token 4(s + 1) + q).  bf16 words
+// hold dims 2k, 2k + 1 in word k: one byte permute per result.  fp8 words
+// hold dims 4k .. 4k + 3 in word k: one permute pairs the two tokens' codes
+// of two dims, and each half of it widens to one result.
+// fp8 words c0 (token t0) and c1 (token t1) holding dims d .. d + 3: bytes
+// (t0 d, t1 d, t0 d + 1, t1 d + 1) and (t0 d + 2, t1 d + 2, t0 d + 3, t1 d + 3)
+// widen to the bf16 pairs of dims d, d + 1 (lo) and d + 2, d + 3 (hi).
+__device__ __forceinline__ void fp8_pairs(uint32_t c0, uint32_t c1, u32x2& lo, u32x2& hi) {
+  lo = fp8x4_to_bf16x4(__builtin_amdgcn_perm(c1, c0, 0x05010400u));
+  hi = fp8x4_to_bf16x4(__builtin_amdgcn_perm(c1, c0, 0x07030602u));
+}
+
+template <int KV>
+__device__ __forceinline__ void v_pairs(const u32x4& w0, const u32x4& w1, u32x2 (&out)[4]) {
+  if constexpr (KV == DT_BF16) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      out[k].x = __builtin_amdgcn_perm(w1[k], w0[k], 0x05040100u);  // dim 2k
+      out[k].y = __builtin_amdgcn_perm(w1[k], w0[k], 0x07060302u);  // dim 2k + 1
+    }
+  } else {
+    fp8_pairs(w0.x, w1.x, out[0], out[1]);  // dims 0 .. 3 of the lane's 8
+    fp8_pairs(w0.y, w1.y, out[2], out[3]);  // dims 4 .. 7
+  }
+}
+
+template <int KV, int NG>
 __device__ __forceinline__ void softmax_pv_pair(const Half<NG>& a, const Half<NG>& b,
                                                 Acc<NG>& acc) {
-  // V operands for the 8 dim groups: A row c = dim 8c + n
+  // V operands for the 8 dim groups: A row c = dim 8c + n; pairs (tokens
+  // q, q + 4) and (q + 8, q + 12) of each block
+  u32x2 pa01[4], pa23[4], pb01[4], pb23[4];
+  v_pairs<KV>(a.vb[0], a.vb[1], pa01);
+  v_pairs<KV>(a.vb[2], a.vb[3], pa23);
+  v_pairs<KV>(b.vb[0], b.vb[1], pb01);
+  v_pairs<KV>(b.vb[2], b.vb[3], pb23);
   u32x4 va[8];
 #pragma unroll
   for (int nn = 0; nn < 8; ++nn) {
-    const uint32_t sel = (nn & 1) ? 0x07060302u : 0x05040100u;
     const int k = nn >> 1;
-    va[nn].x = __builtin_amdgcn_perm(a.vb[1][k], a.vb[0][k], sel);
-    va[nn].y = __builtin_amdgcn_perm(a.vb[3][k], a.vb[2][k], sel);
-    va[nn].z = __builtin_amdgcn_perm(b.vb[1][k], b.vb[0][k], sel);
-    va[nn].w = __builtin_amdgcn_perm(b.vb[3][k], b.vb[2][k], sel);
+    const bool odd = nn & 1;
+    va[nn].x = odd ? pa01[k].y : pa01[k].x;
+    va[nn].y = odd ? pa23[k].y : pa23[k].x;
+    va[nn].z = odd ? pb01[k].y : pb01[k].x;
+    va[nn].w = odd ? pb23[k].y : pb23[k].x;
   }
 #pragma unroll
   for (int G = 0; G < NG; ++G) {
@@ -440,7 +482,7 @@ __device__ __forceinline__ void run_blocks(const DecodeArgs& a, const LaneMap& L
         // even steps keep their scores; odd steps complete the pair
         qk_block<KV, NG>(a.scale_log2, L, lds_k, qop, kbuf[u], vbuf[u], valid, full, lim,
                          half[u & 1]);
-        if (u & 1) softmax_pv_pair<NG>(half[0], half[1], acc);
+        if (u & 1) softmax_pv_pair<KV, NG>(half[0], half[1], acc);
       }
     }
   }
