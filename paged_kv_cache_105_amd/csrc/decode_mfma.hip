@@ -171,9 +171,9 @@ __global__ __launch_bounds__(64, 2) void decode_mfma_kernel(DecodeArgs a) {
 // The walk is one stream of loads over the whole chunk.  It moves in groups
 // of up to 64 blocks of one sequence (one table entry per lane); when a group
 // starts, the next group's table entries (and, for a new sequence, its
-// length) are requested, and the last step of a group already loads the next
-// group's first block, so neither a table window nor a change of sequence
-// lets the loads run dry.
+// length) are requested, and the last two steps of a group already load the
+// next group's first two blocks, so neither a table window nor a change of
+// sequence lets the loads run dry.
 
 typedef const __attribute__((address_space(4))) int32_t* const_i32p;
 

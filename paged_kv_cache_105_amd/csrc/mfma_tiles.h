@@ -27,7 +27,9 @@
 //     (n = 0..7) uses A-operand row c for dim 8c + n and k-index 8q + i for
 //     token q + 4i of block a (i < 4) or q + 4(i - 4) of block b (i >= 4):
 //     lane l already holds V[q + 4i][8c + n] of both blocks from load
-//     s = i, so V needs one byte-permute per pair of values and no LDS.
+//     s = i, so V needs one byte-permute per pair of values and no LDS
+//     (fp8: one permute pairs two tokens' codes of two dims, and the
+//     widening conversion turns each half into one operand word).
 //     (The K = 16 product runs at half the K = 32 product's rate on gfx950.)
 //   * The accumulator of step n gives lane l column c, dims 32q + 8i + n:
 //     every lane owns one column's running max and sum, and rescales its own
