@@ -320,6 +320,26 @@ def test_balanced_split_edge_cases(lens):
     assert np.all(np.isfinite(out))
 
 
+@pytest.mark.parametrize("B", [8192, 8193])
+def test_largest_batches(B):
+    # 8192 requests is the largest batch the flat kernel takes (its block
+    # prefix over requests lives in LDS); one more goes to the fixed-partition
+    # kernel, and asking for the flat kernel then is refused
+    rng = np.random.default_rng(B)
+    lens = rng.integers(1, 49, size=B).tolist()
+    w = make_workload("llama8b", lens_after=lens, H_Q=8, H_KV=2)
+    if B > 8192:
+        with pytest.raises(pkv.PkvError):
+            gpu_step(w, variant=pkv.PKV_VARIANT_MFMA)
+    _, _, out = gpu_step(w)
+    assert np.all(np.isfinite(out))
+    req = [0, 1, B // 2, B - 2, B - 1]
+    _, _, ref = oracle_step(w, _np(w), requests=req)
+    e = _err(out, ref, req)
+    _log(f"B={B} err={e:.2e}")
+    assert e <= TOL
+
+
 def test_run_to_run_bitwise_deterministic():
     w = make_workload("llama8b", lens_after=[5, 900, 2000], H_Q=32, H_KV=8)
     a = gpu_step(w)[2]
