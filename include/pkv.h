@@ -27,7 +27,9 @@
  *   k_scale, v_scale : [num_blocks][H_KV] float, fp8 only (stored value =
  *                      E4M3 code value * scale), NULL otherwise
  *   block_table      : [B][max_blocks_per_seq] int32, row-major; entries
- *                      past a request's last block are never read
+ *                      past a request's last block are never read;
+ *                      max_blocks_per_seq * block_size <= INT32_MAX
+ *                      (positions are int32), else PKV_ERR_INVALID_ARG
  *   context_lens     : [B] int32, positions after the append, >= 1
  *   q                : [B][H_Q][d_h] of q_dtype
  *   k_new, v_new     : [B][H_KV][d_h] of q_dtype

@@ -175,6 +175,9 @@ int check_attention_args(const float* out, const void* q, int q_dtype, const voi
   if (B < 1 || H_Q < 1 || H_KV < 1 || H_Q % H_KV || d_h < 1 || d_h > kMaxDh || block_size < 1 ||
       num_blocks < 1 || max_blocks_per_seq < 1 || max_context_len < 1)
     return PKV_ERR_INVALID_ARG;
+  // positions are int32: a table row may span at most INT32_MAX of them
+  if (static_cast<long long>(max_blocks_per_seq) * block_size > INT32_MAX)
+    return PKV_ERR_INVALID_ARG;
   if (static_cast<long long>(max_context_len) >
       static_cast<long long>(max_blocks_per_seq) * block_size)
     return PKV_ERR_INVALID_ARG;
@@ -239,6 +242,8 @@ int check_append_args(const void* k_new, const void* v_new, int in_dtype, void* 
   if (B < 1 || H_KV < 1 || d_h < 1 || d_h > kMaxDh || block_size < 1 || num_blocks < 1 ||
       max_blocks_per_seq < 1)
     return PKV_ERR_INVALID_ARG;
+  if (static_cast<long long>(max_blocks_per_seq) * block_size > INT32_MAX)
+    return PKV_ERR_INVALID_ARG;  // positions are int32
   if (kv_dtype == PKV_FP8_E4M3 && (!k_scale || !v_scale)) return PKV_ERR_INVALID_ARG;
   const bool pair_ok = (in_dtype == kv_dtype) || kv_dtype == PKV_FP8_E4M3;
   if (!pair_ok) return PKV_ERR_UNSUPPORTED;

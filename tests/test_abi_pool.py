@@ -1,7 +1,8 @@
 """CPU tests of the C-ABI library: it loads, exports every function the
 header declares, and its host block pool follows the Table 21.1 walk (page
 1, section 21.5) and agrees with the oracle's pool model on random operation
-sequences.  No device function is called here."""
+sequences.  No device function is called here, except with arguments that
+its host-side checks reject before any launch."""
 
 import ctypes as C
 import json
@@ -224,3 +225,26 @@ def test_alloc_n_matches_oracle():
     ref.release([7, 2, 9])
     assert lib.alloc_n(10) == ref.alloc_n(10)
     assert lib.num_free() == 0
+
+
+def test_table_row_wider_than_int32_positions_is_rejected():
+    # Positions are int32, so a table row may span at most INT32_MAX of them
+    # (max_blocks_per_seq * block_size); the check runs on the host before
+    # anything is launched.  The pointers are placeholders: the test runs only
+    # where no device is present, so no call here can reach a device.  One
+    # block less passes the checks and then fails at the launch.
+    torch = pytest.importorskip("torch")
+    if torch.cuda.device_count() > 0:
+        pytest.skip("placeholder pointers: runs only where no device is present")
+    lib = pkv.load()
+    p = C.c_void_p(1 << 12)
+    wide = (1 << 31) // 16  # 2^27 blocks of 16 positions = 2^31 positions
+    for mbps, want in ((wide, "invalid_arg"), (wide - 1, "hip")):
+        st = lib.pkv_kv_append(p, p, pkv.PKV_BF16, p, p, pkv.PKV_BF16, None, None, p, mbps, p,
+                               4, 8, 128, 16, 100, None)
+        assert pkv._lib.STATUS_NAMES[st] == want
+        st = lib.pkv_paged_decode_attention(p, p, pkv.PKV_BF16, p, p, pkv.PKV_BF16, None, None,
+                                            p, mbps, p, 16, 4, 32, 8, 128, 16, 100,
+                                            C.c_float(0.1), 0, None, 0, None)
+        assert pkv._lib.STATUS_NAMES[st] in ((want,) if want == "invalid_arg"
+                                             else ("hip", "workspace"))
