@@ -63,6 +63,7 @@ def oracle_step(w, d, requests=None):
     (dict(B=5, kv_dtype="fp8_e4m3"), 75),
     (dict(B=4, H_Q=8, H_KV=8), 75),                         # g = 1
     (dict(B=3, H_Q=32, H_KV=1), 75),                        # g = 32
+    (dict(B=3, H_Q=32, H_KV=1, kv_dtype="fp8_e4m3"), 75),   # g = 32, fp8
     (dict(B=7, shared_tokens=64, private_tokens=1, offset_hi=40), 4),   # short private parts
 ], ids=lambda x: str(x)[:40])
 def test_cascade_step_matches_oracle(kw, shared):
