@@ -447,8 +447,9 @@ int pkv_swap_in(void* k_cache, void* v_cache, int kv_dtype, float* k_scale, floa
                 const int32_t* blocks, int32_t n, int32_t H_KV, int32_t d_h, int32_t block_size,
                 int32_t num_blocks, const void* records, pkv_stream_t stream);
 
-/* Kernel selection for the attention calls (process-wide, not
- * thread-safe).  AUTO uses the MFMA kernel with the balanced per-wave split
+/* Kernel selection for the attention calls (process-wide; any thread may
+ * set or read it, and a call uses the value current when it plans; a plan
+ * and the attention call it sizes must see the same value).  AUTO uses the MFMA kernel with the balanced per-wave split
  * where it applies and the generic VALU kernel otherwise; GENERIC, MFMA
  * (balanced split) and MFMA_PARTITION (fixed partitions) force one, and
  * return UNSUPPORTED from the plan and attention calls outside their

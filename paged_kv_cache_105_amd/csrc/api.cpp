@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdint>
 #include <cstdlib>
@@ -49,7 +50,7 @@ hipError_t launch_combine(float* out, const int32_t* context_lens, const void* w
 
 namespace {
 
-int g_variant = PKV_VARIANT_AUTO;
+std::atomic<int> g_variant{PKV_VARIANT_AUTO};  // read and set from any thread
 
 constexpr int kMaxDh = 256;
 constexpr int kMaxGenericPartition = 256;
@@ -131,7 +132,7 @@ int make_plan(int B, int H_Q, int H_KV, int d_h, int block_size, int max_context
   plan->waves = 0;
 
   const bool mfma_ok = pkv::mfma_supports(q_dtype, kv_dtype, d_h, block_size, g);
-  switch (g_variant) {
+  switch (g_variant.load(std::memory_order_relaxed)) {
     case PKV_VARIANT_GENERIC:
       plan->kernel = K_GENERIC;
       break;
@@ -219,11 +220,10 @@ const char* pkv_status_string(int status) {
 int pkv_abi_version(void) { return 2; }
 
 int pkv_set_decode_variant(int variant) {
-  const int prev = g_variant;
   if (variant == PKV_VARIANT_AUTO || variant == PKV_VARIANT_GENERIC ||
       variant == PKV_VARIANT_MFMA || variant == PKV_VARIANT_MFMA_PARTITION)
-    g_variant = variant;
-  return prev;
+    return g_variant.exchange(variant, std::memory_order_relaxed);
+  return g_variant.load(std::memory_order_relaxed);
 }
 
 }  // extern "C"
@@ -326,7 +326,7 @@ int pkv_paged_chunk_attention(float* out, const void* q, int q_dtype, const void
   a.query_start = query_start;
   a.total_q = total_q;
   const hipStream_t s = static_cast<hipStream_t>(stream);
-  const bool mfma = g_variant != PKV_VARIANT_GENERIC &&
+  const bool mfma = g_variant.load(std::memory_order_relaxed) != PKV_VARIANT_GENERIC &&
                     pkv::chunk_mfma_supports(q_dtype, kv_dtype, d_h, block_size);
   return hip_status(mfma ? pkv::launch_chunk_mfma(kv_dtype, max_q_len, a, s)
                          : pkv::launch_chunk_generic(q_dtype, kv_dtype, a, s));

@@ -248,3 +248,27 @@ def test_table_row_wider_than_int32_positions_is_rejected():
                                             C.c_float(0.1), 0, None, 0, None)
         assert pkv._lib.STATUS_NAMES[st] in ((want,) if want == "invalid_arg"
                                              else ("hip", "workspace"))
+
+
+def test_decode_variant_selector():
+    # a host-only setting: returns the previous value, ignores unknown values
+    # and is safe to set from several threads at once
+    import threading
+    prev = pkv.set_decode_variant(pkv.PKV_VARIANT_GENERIC)
+    try:
+        assert pkv.set_decode_variant(pkv.PKV_VARIANT_MFMA) == pkv.PKV_VARIANT_GENERIC
+        assert pkv.set_decode_variant(99) == pkv.PKV_VARIANT_MFMA
+        assert pkv.set_decode_variant(pkv.PKV_VARIANT_MFMA) == pkv.PKV_VARIANT_MFMA
+
+        def flip(v):
+            for _ in range(2000):
+                assert pkv.set_decode_variant(v) in (pkv.PKV_VARIANT_AUTO, pkv.PKV_VARIANT_GENERIC,
+                                                     pkv.PKV_VARIANT_MFMA,
+                                                     pkv.PKV_VARIANT_MFMA_PARTITION)
+        ts = [threading.Thread(target=flip, args=(v,)) for v in (0, 1, 2, 3)]
+        for t in ts:
+            t.start()
+        for t in ts:
+            t.join()
+    finally:
+        pkv.set_decode_variant(prev)
