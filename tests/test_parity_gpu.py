@@ -6,6 +6,8 @@
   many blocks, several partitions and ragged tails, for both kernels (generic
   VALU and MFMA), every group size 1..32, bf16 and fp8 caches, and at the
   full sizes of the measured workloads on sampled requests;
+* softmax scales at both ends (1e-4: near-uniform weights; 30: a near
+  argmax), bf16 and fp8 caches, every kernel;
 * paging invariants, bitwise: physical permutation, shared vs private prefix
   copies, NaN / huge values in every unused slot;
 * fp8 codec: all 65,536 bf16 inputs x 4 scales through kv_append, and all
@@ -292,6 +294,32 @@ def test_generic_other_head_dims():
         e = _err(out, ref)
         _log(f"d_h={d_h} bs={bs} err={e:.2e}")
         assert e <= TOL
+
+
+class _Scaled:
+    """A workload seen with another softmax scale."""
+
+    def __init__(self, w, scale):
+        self._w, self.softmax_scale = w, scale
+
+    def __getattr__(self, name):
+        return getattr(self._w, name)
+
+
+@pytest.mark.parametrize("variant", VARIANTS, ids=VIDS)
+@pytest.mark.parametrize("name", ["llama8b", "fp8_gqa"])
+@pytest.mark.parametrize("scale", [1e-4, 30.0])
+def test_extreme_softmax_scales(variant, name, scale):
+    # near-uniform weights (the output tends to the mean of V) and a near
+    # argmax (one value row wins by hundreds of log units); the bf16 MFMA
+    # path folds the scale into the exponent, fp8 into each block's product
+    kw = dict(H_Q=32, H_KV=8) if name == "llama8b" else {}
+    w = _Scaled(make_workload(name, lens_after=[1, 17, 300, 2049], **kw), scale)
+    _, _, out = gpu_step(w, variant=variant)
+    _, _, ref = oracle_step(w, _np(w))
+    e = _err(out, ref)
+    _log(f"{name} scale={scale} variant={variant} err={e:.2e}")
+    assert e <= TOL
 
 
 def test_split_partitions_agree_with_one_partition():
