@@ -8,6 +8,8 @@
   full sizes of the measured workloads on sampled requests;
 * softmax scales at both ends (1e-4: near-uniform weights; 30: a near
   argmax), bf16 and fp8 caches, every kernel;
+* out-of-range lengths and block ids on the device stay contained: the other
+  requests still match the oracle;
 * paging invariants, bitwise: physical permutation, shared vs private prefix
   copies, NaN / huge values in every unused slot;
 * fp8 codec: all 65,536 bf16 inputs x 4 scales through kv_append, and all
@@ -319,6 +321,38 @@ def test_extreme_softmax_scales(variant, name, scale):
     _, _, ref = oracle_step(w, _np(w))
     e = _err(out, ref)
     _log(f"{name} scale={scale} variant={variant} err={e:.2e}")
+    assert e <= TOL
+
+
+class _Override:
+    """A workload with some of its device inputs replaced."""
+
+    def __init__(self, w, **fields):
+        self._w = w
+        self.__dict__.update(fields)
+
+    def __getattr__(self, name):
+        return getattr(self._w, name)
+
+
+@pytest.mark.parametrize("variant", VARIANTS, ids=VIDS)
+def test_out_of_range_device_values_stay_contained(variant):
+    # Device-side values are trusted but never followed outside the caller's
+    # buffers: a length of 0, -5 or beyond the table row, and block ids past
+    # the pool or negative, only make that request's result unspecified.  The
+    # other requests still match the oracle, and none of them is disturbed.
+    lens = [5, 300, 900, 17, 2000, 64, 33]
+    w = make_workload("llama8b", lens_after=lens, H_Q=32, H_KV=8)
+    good = [0, 2, 4]
+    _, _, ref = oracle_step(w, _np(w), requests=good)
+    cl = w.context_lens.clone()
+    cl[1], cl[3], cl[6] = 0, 10 ** 6, -5
+    bt = w.block_table.clone()
+    bt[5, 1], bt[5, 2] = w.num_blocks + 7, -3
+    bad = _Override(w, context_lens=cl, block_table=bt)
+    _, _, out = gpu_step(bad, variant=variant)
+    e = _err(out, ref, good)
+    _log(f"out-of-range values variant={variant}: err on the other requests {e:.2e}")
     assert e <= TOL
 
 
