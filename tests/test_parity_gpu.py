@@ -350,10 +350,20 @@ def test_out_of_range_device_values_stay_contained(variant):
     bt = w.block_table.clone()
     bt[5, 1], bt[5, 2] = w.num_blocks + 7, -3
     bad = _Override(w, context_lens=cl, block_table=bt)
-    _, _, out = gpu_step(bad, variant=variant)
-    e = _err(out, ref, good)
-    _log(f"out-of-range values variant={variant}: err on the other requests {e:.2e}")
-    assert e <= TOL
+    # pools: only requests with a valid length and a valid last block (0, 2,
+    # 4 and 5) get their row; every other byte stays as it was
+    sel = [0, 2, 4, 5]
+    rk, rv = paged.append(as_numpy(w.k_cache[0]), as_numpy(w.v_cache[0]), w.kv_dtype,
+                          as_numpy(w.k_new[0])[sel], as_numpy(w.v_new[0])[sel], w.q_dtype,
+                          as_numpy(bt)[sel], as_numpy(cl)[sel], w.block_size)
+    # the append kernel + attention, then the decode step (whose MFMA kernels
+    # do the append inside the launch)
+    for run in (lambda: gpu_step(bad, variant=variant), lambda: _fused_step(bad, variant)):
+        kc, vc, out = run()
+        e = _err(out, ref, good)
+        _log(f"out-of-range values variant={variant}: err on the other requests {e:.2e}")
+        assert e <= TOL
+        assert np.array_equal(as_numpy(kc), rk) and np.array_equal(as_numpy(vc), rv)
 
 
 def test_split_partitions_agree_with_one_partition():
