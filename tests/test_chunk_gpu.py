@@ -11,7 +11,8 @@ C ABI against the float64 oracle.
   21.3: a twelve-token prompt in chunks of four gives the outputs of the
   whole prompt as one chunk;
 * a chunk of one token per request agrees with the decode kernel;
-* unused slots holding NaN are never read;
+* unused slots holding NaN are never read; out-of-range lengths and block ids
+  on the device stay contained;
 * page 3 "xf_kv_cache", "End-to-end flow", at full size: 64 requests share a
   75-block prefix and process 600 new tokens each; sampled requests.
 """
@@ -215,6 +216,45 @@ def test_chunk_unused_slots_never_read(variant):
                 vc[p, :, r] = float("nan")
     _, _, out = gpu_chunk(w, variant, kc=kc, vc=vc)
     assert _err(out, ref) <= TOL
+
+
+class _Override:
+    """A workload with some of its device inputs replaced."""
+
+    def __init__(self, w, **fields):
+        self._w = w
+        self.__dict__.update(fields)
+
+    def __getattr__(self, name):
+        return getattr(self._w, name)
+
+
+@pytest.mark.parametrize("variant", KERNELS, ids=KIDS)
+def test_chunk_out_of_range_device_values_stay_contained(variant):
+    # lengths of 0 (shorter than the chunk), -5 and beyond the table row, and
+    # block ids past the pool or negative: those requests' rows are
+    # unspecified, their chunks are not appended, and the other requests
+    # still match the oracle with bit-exact pools
+    w = make_workload("llama8b", lens_after=[40, 17, 300, 77, 64, 33],
+                      new_tokens=[20, 17, 129, 1, 16, 2], H_Q=32, H_KV=8)
+    d = _np(w)
+    good = [0, 2]
+    _, _, ref = oracle_chunk(w, d, requests=good)
+    cl = w.context_lens.clone()
+    cl[1], cl[3], cl[5] = 0, 10 ** 6, -5
+    bt = w.block_table.clone()
+    bt[4, 1], bt[4, 2] = w.num_blocks + 7, -3   # request 4 appends into its block 3
+    sel = [0, 2, 4]
+    rows = _rows(d, sel)
+    qs = np.concatenate([[0], np.cumsum([d["qs"][b + 1] - d["qs"][b] for b in sel])])
+    rk, rv = paged.append_chunk(as_numpy(w.k_cache[0]), as_numpy(w.v_cache[0]), w.kv_dtype,
+                                d["k_new"][rows], d["v_new"][rows], w.q_dtype,
+                                as_numpy(bt)[sel], as_numpy(cl)[sel], qs, w.block_size)
+    kc, vc, out = gpu_chunk(_Override(w, context_lens=cl, block_table=bt), variant)
+    e = _err(out, ref, _rows(d, good))
+    _log(f"chunk out-of-range values variant={variant}: err on the other requests {e:.2e}")
+    assert e <= TOL
+    assert np.array_equal(as_numpy(kc), rk) and np.array_equal(as_numpy(vc), rv)
 
 
 def test_prefix_hit_full_size_sampled():
