@@ -156,13 +156,15 @@ def _ceil_div(a, b):
     return -(-a // b)
 
 
-def make_workload(name: str, device="cpu", seed=None, **overrides) -> Workload:
+def make_workload(name: str, device="cpu", seed=None, values=True, **overrides) -> Workload:
     """Draw one decode step of the named workload on ``device``.
 
     ``overrides`` may change B, layers, H_KV, context lengths (``lens_after``
     as a list), new tokens per request (``new_tokens``, a list) and the pool
     factor (``pool_factor``) to make small variants for tests; everything
-    else keeps the named workload's recipe."""
+    else keeps the named workload's recipe.  ``values=False`` stops after
+    the lengths and block tables (the pools, scales and new rows stay
+    empty); the lengths and tables are the same as with values."""
     cfg = dict(CONFIGS[name])
     lens_after = overrides.pop("lens_after", None)
     new_tokens = overrides.pop("new_tokens", None)
@@ -218,6 +220,8 @@ def make_workload(name: str, device="cpu", seed=None, **overrides) -> Workload:
                  query_start=qstart.to(torch.int32).to(device), total_q=total_q,
                  max_q_len=max(new_tokens))
 
+    if not values:
+        return w
     # 3.. values, per layer, on the target device
     dgen = torch.Generator(device=device)
     dgen.manual_seed((cfg["seed"] if seed is None else seed) * 1000 + 17)

@@ -1,0 +1,101 @@
+"""Byte accounting of one decode step, pinned to the pages' figures.
+
+Page 1, "KV cache: Generation state, latency, and allocation", section 21.1,
+Eq. 21.2: the payload is 2 x layers x requests x KV heads x positions x d_h x
+bytes per scalar.  Applied to one decode step of one layer, request b reads
+its n_b positions (after the append) of K and V for every KV head.  Page 2,
+"KV Cache Explained", section "How much GPU memory does the KV cache use?",
+prints the per-token figure for the Llama-3.1-8B-style shape (32 layers, 8
+KV heads, d_h 128, bf16): 131,072 bytes, and 524,288 bytes with 32 KV heads;
+section "What changes when you use FP8 KV": one byte per element instead of
+two.
+
+Two implementations of the per-step count exist and must agree with these
+figures and with each other: the oracle's ``decode_step_kv_read_bytes`` and
+the measurement's ``metrics.attention_bytes`` (the denominator of every GB/s
+figure the benchmark reports).
+"""
+
+import json
+import os
+
+import pytest
+
+from oracle import kvbytes
+from paged_kv_cache_105_amd import metrics
+from paged_kv_cache_105_amd.workloads import make_workload
+
+GOLD = json.load(open(os.path.join(os.path.dirname(__file__), "golden",
+                                   "page_arithmetic.json")))
+
+
+def _per_token(kv_heads):
+    """Bytes per token of the page's 32-layer figure for this KV head count."""
+    for case in GOLD["growth_per_token"]:
+        layers, batch, heads, d_h, s = case["args"]
+        if (layers, batch, heads, d_h, s) == (32, 1, kv_heads, 128, 2):
+            return case["bytes"]
+    raise KeyError(kv_heads)
+
+
+# bytes per position per layer: the page's per-token figure / 32 layers, and
+# half of it for one-byte fp8 elements; 1 KV head is an eighth of 8 heads
+PER_POS = {
+    ("bf16", 8): _per_token(8) // 32,
+    ("fp8_e4m3", 8): _per_token(8) // 32 // 2,
+    ("fp8_e4m3", 32): _per_token(32) // 32 // 2,
+    ("fp8_e4m3", 1): _per_token(8) // 32 // 2 // 8,
+}
+
+
+@pytest.mark.parametrize("name", ["llama8b", "long32k", "shared_prefix", "fp8_mqa", "fp8_gqa",
+                                  "fp8_mha"])
+def test_step_kv_bytes_follow_the_per_token_figure(name):
+    kw = dict(layers=1, H_KV=8) if name == "shared_prefix" else {}
+    w = make_workload(name, values=False, **kw)
+    lens = [int(n) for n in w.context_lens]
+    want = PER_POS[(w.kv_dtype, w.H_KV)] * sum(lens)
+    s = metrics.DTYPE_BYTES[w.kv_dtype]
+    assert kvbytes.decode_step_kv_read_bytes(lens, w.H_KV, w.d_h, s) == want
+    att = metrics.attention_bytes(lens, w.H_Q, w.H_KV, w.d_h, w.block_size, w.kv_dtype,
+                                  w.q_dtype)
+    assert att["kv"] == want
+
+
+def test_long_context_layer_is_one_gib():
+    # 8 requests x 32,768 positions: page 2's 4 GiB per 32,768-token history
+    # (32 layers) is 128 MiB per layer and request, 1 GiB for the batch
+    w = make_workload("long32k", values=False)
+    lens = [int(n) for n in w.context_lens]
+    per_request_all_layers = _per_token(8) * 32768
+    assert per_request_all_layers == 4 * kvbytes.GIB
+    assert kvbytes.decode_step_kv_read_bytes(lens, 8, 128, 2) == 8 * per_request_all_layers // 32
+    assert metrics.attention_bytes(lens, 32, 8, 128, 16, "bf16", "bf16")["kv"] == kvbytes.GIB
+
+
+def test_per_request_sum_equals_eq_21_2_for_equal_lengths():
+    # with every n_b equal the per-request sum is Eq. 21.2 with batch B
+    lens = [777] * 5
+    assert kvbytes.decode_step_kv_read_bytes(lens, 4, 64, 2) == \
+        kvbytes.payload_bytes(1, 5, 4, 777, 64, 2)
+
+
+def test_attention_bytes_other_terms_by_hand():
+    # lengths 1, 16, 17 in 16-slot blocks: 1 + 1 + 2 blocks; H_Q 4, H_KV 2,
+    # d_h 8, fp8 cache with bf16 queries
+    att = metrics.attention_bytes([1, 16, 17], 4, 2, 8, 16, "fp8_e4m3", "bf16")
+    assert att["kv"] == 2 * 2 * 8 * 1 * (1 + 16 + 17)       # 1088
+    assert att["scales"] == 2 * 2 * 4 * 4                   # K and V scale per block and head
+    assert att["q"] == 3 * 4 * 8 * 2
+    assert att["out"] == 3 * 4 * 8 * 4
+    assert att["table"] == 4 * 4 + 3 * 4                    # block ids + lengths
+    assert att["total"] == 1088 + 64 + 192 + 384 + 28
+    # bf16 caches carry no scales
+    assert metrics.attention_bytes([5], 2, 1, 8, 4, "bf16", "bf16")["scales"] == 0
+
+
+def test_append_bytes_by_hand():
+    # new K and V rows read (bf16) and written (fp8), one scale each read,
+    # and the table entry and length of every request
+    assert metrics.append_bytes(3, 2, 8, "fp8_e4m3", "bf16") == \
+        2 * 3 * 2 * 8 * (2 + 1) + 2 * 3 * 2 * 4 + 8 * 3
