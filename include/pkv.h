@@ -271,6 +271,21 @@ int pkv_decode_plan(int32_t B, int32_t H_Q, int32_t H_KV, int32_t d_h, int32_t b
                     int kv_dtype, int32_t* partition_tokens_out, int32_t* max_partitions_out,
                     size_t* workspace_bytes);
 
+/* Workspace size for pkv_paged_decode_attention, pkv_decode_partitions and
+ * pkv_decode_step with these shapes and dtypes: the largest size any kernel
+ * variant needs (the plan above gives the size of the variant selected at
+ * the time of that call only), so a workspace of this size serves every
+ * call with these arguments whatever pkv_set_decode_variant holds when it
+ * runs.  Sizes are for the device current at the call (the balanced split
+ * has one chunk per wave the device holds at once); a call on a device
+ * that needs more returns PKV_ERR_WORKSPACE and launches nothing.
+ * INVALID_ARG for invalid shapes or a NULL workspace_bytes; UNSUPPORTED if
+ * no kernel takes the shapes. */
+int pkv_decode_workspace_size(int32_t B, int32_t H_Q, int32_t H_KV, int32_t d_h,
+                              int32_t block_size, int32_t max_context_len,
+                              int32_t partition_tokens, int q_dtype, int kv_dtype,
+                              size_t* workspace_bytes);
+
 /* Paged decode attention (page 1 section 21.1: every query head normalises
  * its scores over the request's cached keys, its own new key included, and
  * mixes the values; section 21.5: attention follows the block table).  For

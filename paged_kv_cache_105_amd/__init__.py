@@ -15,7 +15,7 @@ from . import _lib
 from ._lib import (PKV_BF16, PKV_F32, PKV_FP8_E4M3, PKV_VARIANT_AUTO, PKV_VARIANT_GENERIC,
                    PKV_VARIANT_MFMA, PKV_VARIANT_MFMA_PARTITION, PkvError, check, load)
 
-__all__ = ["kv_append", "copy_blocks", "decode_plan", "paged_decode_attention", "decode_partitions",
+__all__ = ["kv_append", "copy_blocks", "decode_plan", "decode_workspace_size", "paged_decode_attention", "decode_partitions",
            "combine_partitions", "set_decode_variant", "BlockPool", "PkvError", "load",
            "prefix_root", "block_hashes", "DIGEST_BYTES", "kv_append_chunk",
            "paged_chunk_attention", "swap_record_bytes", "swap_out", "swap_in", "decode_step",
@@ -175,6 +175,17 @@ def decode_plan(B, H_Q, H_KV, d_h, block_size, max_context_len, partition_tokens
                                  C.byref(parts), C.byref(ws)),
           "pkv_decode_plan")
     return pt.value, parts.value, ws.value
+
+
+def decode_workspace_size(B, H_Q, H_KV, d_h, block_size, max_context_len, partition_tokens=0,
+                          q_dtype=PKV_BF16, kv_dtype=PKV_BF16):
+    """pkv_decode_workspace_size -> bytes: enough for every kernel variant."""
+    ws = C.c_size_t()
+    check(load().pkv_decode_workspace_size(B, H_Q, H_KV, d_h, block_size, max_context_len,
+                                           partition_tokens, int(q_dtype), int(kv_dtype),
+                                           C.byref(ws)),
+          "pkv_decode_workspace_size")
+    return ws.value
 
 
 def _attn_args(out, q, k_cache, v_cache, block_table, context_lens, max_context_len,

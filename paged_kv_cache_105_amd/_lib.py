@@ -58,6 +58,8 @@ SIGNATURES = {
                                   _vp]),
     "pkv_decode_plan": (C.c_int, [_i32, _i32, _i32, _i32, _i32, _i32, _i32, C.c_int, C.c_int,
                                   _pi32, _pi32, C.POINTER(_sz)]),
+    "pkv_decode_workspace_size": (C.c_int, [_i32, _i32, _i32, _i32, _i32, _i32, _i32, C.c_int,
+                                            C.c_int, C.POINTER(_sz)]),
     "pkv_paged_decode_attention": (C.c_int, [_vp, _vp, C.c_int, _vp, _vp, C.c_int, _vp, _vp,
                                              _vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
                                              _i32, _f, _i32, _vp, _sz, _vp]),

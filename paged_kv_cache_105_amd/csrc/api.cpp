@@ -116,8 +116,13 @@ int flat_waves_cached(int kv_dtype, int g, int B, bool cascade = false) {
   return w;
 }
 
-int make_plan(int B, int H_Q, int H_KV, int d_h, int block_size, int max_context_len,
-              int partition_tokens, int q_dtype, int kv_dtype, Plan* plan) {
+// The variant is read once by each entry point (current_variant) and passed
+// down, so every decision of one call -- plan, kernel, combine -- sees the
+// same value even while another thread changes the setting.
+int current_variant() { return g_variant.load(std::memory_order_relaxed); }
+
+int make_plan(int variant, int B, int H_Q, int H_KV, int d_h, int block_size,
+              int max_context_len, int partition_tokens, int q_dtype, int kv_dtype, Plan* plan) {
   if (B < 1 || H_Q < 1 || H_KV < 1 || H_Q % H_KV || d_h < 1 || d_h > kMaxDh || block_size < 1 ||
       max_context_len < 1 || partition_tokens < 0 || !valid_dtype(q_dtype) ||
       !valid_dtype(kv_dtype))
@@ -132,7 +137,7 @@ int make_plan(int B, int H_Q, int H_KV, int d_h, int block_size, int max_context
   plan->waves = 0;
 
   const bool mfma_ok = pkv::mfma_supports(q_dtype, kv_dtype, d_h, block_size, g);
-  switch (g_variant.load(std::memory_order_relaxed)) {
+  switch (variant) {
     case PKV_VARIANT_GENERIC:
       plan->kernel = K_GENERIC;
       break;
@@ -326,7 +331,7 @@ int pkv_paged_chunk_attention(float* out, const void* q, int q_dtype, const void
   a.query_start = query_start;
   a.total_q = total_q;
   const hipStream_t s = static_cast<hipStream_t>(stream);
-  const bool mfma = g_variant.load(std::memory_order_relaxed) != PKV_VARIANT_GENERIC &&
+  const bool mfma = current_variant() != PKV_VARIANT_GENERIC &&
                     pkv::chunk_mfma_supports(q_dtype, kv_dtype, d_h, block_size);
   return hip_status(mfma ? pkv::launch_chunk_mfma(kv_dtype, max_q_len, a, s)
                          : pkv::launch_chunk_generic(q_dtype, kv_dtype, a, s));
@@ -354,12 +359,36 @@ int pkv_decode_plan(int32_t B, int32_t H_Q, int32_t H_KV, int32_t d_h, int32_t b
                     int32_t* partition_tokens_out, int32_t* max_partitions_out,
                     size_t* workspace_bytes) {
   Plan plan;
-  const int st = make_plan(B, H_Q, H_KV, d_h, block_size, max_context_len, partition_tokens,
-                           q_dtype, kv_dtype, &plan);
+  const int st = make_plan(current_variant(), B, H_Q, H_KV, d_h, block_size, max_context_len,
+                           partition_tokens, q_dtype, kv_dtype, &plan);
   if (st != PKV_OK) return st;
   if (partition_tokens_out) *partition_tokens_out = plan.partition_tokens;
   if (max_partitions_out) *max_partitions_out = plan.max_parts;
   if (workspace_bytes) *workspace_bytes = plan.total;
+  return PKV_OK;
+}
+
+int pkv_decode_workspace_size(int32_t B, int32_t H_Q, int32_t H_KV, int32_t d_h,
+                              int32_t block_size, int32_t max_context_len,
+                              int32_t partition_tokens, int q_dtype, int kv_dtype,
+                              size_t* workspace_bytes) {
+  if (!workspace_bytes) return PKV_ERR_INVALID_ARG;
+  // the largest workspace any kernel variant needs for these shapes, so the
+  // size holds whatever the process-wide variant is when the call runs
+  size_t most = 0;
+  bool any = false;
+  for (const int v : {PKV_VARIANT_AUTO, PKV_VARIANT_GENERIC, PKV_VARIANT_MFMA,
+                      PKV_VARIANT_MFMA_PARTITION}) {
+    Plan plan;
+    const int st = make_plan(v, B, H_Q, H_KV, d_h, block_size, max_context_len,
+                             partition_tokens, q_dtype, kv_dtype, &plan);
+    if (st == PKV_ERR_UNSUPPORTED) continue;
+    if (st != PKV_OK) return st;  // the shapes themselves are invalid
+    most = std::max(most, plan.total);
+    any = true;
+  }
+  if (!any) return PKV_ERR_UNSUPPORTED;
+  *workspace_bytes = most;
   return PKV_OK;
 }
 
@@ -369,7 +398,8 @@ namespace {
 
 // The partition launch; with k_new / v_new set (MFMA kernels only) the
 // owning waves also append the new token (see pkv_decode_step).
-int decode_launch(const void* k_new, const void* v_new, float* out, const void* q, int q_dtype,
+int decode_launch(int variant, Plan* plan_out, const void* k_new, const void* v_new, float* out,
+                  const void* q, int q_dtype,
                   const void* k_cache, const void* v_cache, int kv_dtype, const float* k_scale,
                   const float* v_scale, const int32_t* block_table, int32_t max_blocks_per_seq,
                   const int32_t* context_lens, int32_t max_context_len, int32_t B, int32_t H_Q,
@@ -381,9 +411,10 @@ int decode_launch(const void* k_new, const void* v_new, float* out, const void* 
                                 B, H_Q, H_KV, d_h, block_size, num_blocks, softmax_scale);
   if (st != PKV_OK) return st;
   Plan plan;
-  st = make_plan(B, H_Q, H_KV, d_h, block_size, max_context_len, partition_tokens, q_dtype,
-                 kv_dtype, &plan);
+  st = make_plan(variant, B, H_Q, H_KV, d_h, block_size, max_context_len, partition_tokens,
+                 q_dtype, kv_dtype, &plan);
   if (st != PKV_OK) return st;
+  if (plan_out) *plan_out = plan;
   if (plan.total > 0 && (!workspace || workspace_bytes < plan.total)) return PKV_ERR_WORKSPACE;
   if (reinterpret_cast<uintptr_t>(workspace) & 15) return PKV_ERR_INVALID_ARG;
   // a workspace too small to hold the header is not used at all
@@ -444,10 +475,10 @@ int pkv_decode_partitions(float* out, const void* q, int q_dtype, const void* k_
                           int32_t d_h, int32_t block_size, int32_t num_blocks,
                           float softmax_scale, int32_t partition_tokens, void* workspace,
                           size_t workspace_bytes, pkv_stream_t stream) {
-  return decode_launch(nullptr, nullptr, out, q, q_dtype, k_cache, v_cache, kv_dtype, k_scale,
-                       v_scale, block_table, max_blocks_per_seq, context_lens, max_context_len, B,
-                       H_Q, H_KV, d_h, block_size, num_blocks, softmax_scale, partition_tokens,
-                       workspace, workspace_bytes, stream);
+  return decode_launch(current_variant(), nullptr, nullptr, nullptr, out, q, q_dtype, k_cache,
+                       v_cache, kv_dtype, k_scale, v_scale, block_table, max_blocks_per_seq,
+                       context_lens, max_context_len, B, H_Q, H_KV, d_h, block_size, num_blocks,
+                       softmax_scale, partition_tokens, workspace, workspace_bytes, stream);
 }
 
 int pkv_combine_partitions(float* out, const int32_t* context_lens, int32_t max_context_len,
@@ -480,14 +511,12 @@ int pkv_paged_decode_attention(float* out, const void* q, int q_dtype, const voi
                                int32_t d_h, int32_t block_size, int32_t num_blocks,
                                float softmax_scale, int32_t partition_tokens, void* workspace,
                                size_t workspace_bytes, pkv_stream_t stream) {
-  int st = pkv_decode_partitions(out, q, q_dtype, k_cache, v_cache, kv_dtype, k_scale, v_scale,
-                                 block_table, max_blocks_per_seq, context_lens, max_context_len,
-                                 B, H_Q, H_KV, d_h, block_size, num_blocks, softmax_scale,
-                                 partition_tokens, workspace, workspace_bytes, stream);
-  if (st != PKV_OK) return st;
   Plan plan;
-  st = make_plan(B, H_Q, H_KV, d_h, block_size, max_context_len, partition_tokens, q_dtype,
-                 kv_dtype, &plan);
+  const int st = decode_launch(current_variant(), &plan, nullptr, nullptr, out, q, q_dtype,
+                               k_cache, v_cache, kv_dtype, k_scale, v_scale, block_table,
+                               max_blocks_per_seq, context_lens, max_context_len, B, H_Q, H_KV,
+                               d_h, block_size, num_blocks, softmax_scale, partition_tokens,
+                               workspace, workspace_bytes, stream);
   if (st != PKV_OK) return st;
   if (plan.total == 0) return PKV_OK;  // one partition per request: out is final
   return pkv_combine_partitions(out, context_lens, max_context_len, B, H_Q, H_KV, d_h,
@@ -510,10 +539,15 @@ int pkv_decode_step(const void* k_new, const void* v_new, float* out, const void
                          block_table, max_blocks_per_seq, context_lens, B, H_KV, d_h,
                          block_size, num_blocks);
   if (st != PKV_OK) return st;
+  const int variant = current_variant();
   Plan plan;
-  st = make_plan(B, H_Q, H_KV, d_h, block_size, max_context_len, partition_tokens, q_dtype,
-                 kv_dtype, &plan);
+  st = make_plan(variant, B, H_Q, H_KV, d_h, block_size, max_context_len, partition_tokens,
+                 q_dtype, kv_dtype, &plan);
   if (st != PKV_OK) return st;
+  // every check before the first launch: a workspace the attention launch
+  // would refuse must not leave the append done
+  if (plan.total > 0 && (!workspace || workspace_bytes < plan.total)) return PKV_ERR_WORKSPACE;
+  if (reinterpret_cast<uintptr_t>(workspace) & 15) return PKV_ERR_INVALID_ARG;
   const bool aligned =
       ((reinterpret_cast<uintptr_t>(k_new) | reinterpret_cast<uintptr_t>(v_new)) & 15) == 0;
   const bool fused = aligned && pkv::mfma_fuses_append(kv_dtype, H_Q / H_KV) &&
@@ -524,7 +558,8 @@ int pkv_decode_step(const void* k_new, const void* v_new, float* out, const void
                        num_blocks, stream);
     if (st != PKV_OK) return st;
   }
-  st = decode_launch(fused ? k_new : nullptr, fused ? v_new : nullptr, out, q, q_dtype, k_cache,
+  st = decode_launch(variant, nullptr, fused ? k_new : nullptr, fused ? v_new : nullptr, out, q,
+                     q_dtype, k_cache,
                      v_cache, kv_dtype, k_scale, v_scale, block_table, max_blocks_per_seq,
                      context_lens, max_context_len, B, H_Q, H_KV, d_h, block_size, num_blocks,
                      softmax_scale, partition_tokens, workspace, workspace_bytes, stream);
@@ -637,10 +672,11 @@ int cascade_splits(int B, int g, int H_KV, int shared_blocks) {
   return (shared_blocks + bps - 1) / bps;
 }
 
-int cascade_plan(int B, int H_Q, int H_KV, int d_h, int block_size, int max_context_len,
-                 int shared_blocks, int q_dtype, int kv_dtype, Plan* plan, int* splits,
-                 size_t* ws) {
-  int st = make_plan(B, H_Q, H_KV, d_h, block_size, max_context_len, 0, q_dtype, kv_dtype, plan);
+int cascade_plan(int variant, int B, int H_Q, int H_KV, int d_h, int block_size,
+                 int max_context_len, int shared_blocks, int q_dtype, int kv_dtype, Plan* plan,
+                 int* splits, size_t* ws) {
+  int st = make_plan(variant, B, H_Q, H_KV, d_h, block_size, max_context_len, 0, q_dtype,
+                     kv_dtype, plan);
   if (st != PKV_OK) return st;
   if (plan->kernel != K_MFMA_FLAT) return PKV_ERR_UNSUPPORTED;
   if (shared_blocks < 1 || static_cast<long long>(shared_blocks) * block_size > max_context_len)
@@ -663,8 +699,9 @@ int pkv_cascade_plan(int32_t B, int32_t H_Q, int32_t H_KV, int32_t d_h, int32_t 
   Plan plan;
   int splits = 0;
   size_t ws = 0;
-  const int st = cascade_plan(B, H_Q, H_KV, d_h, block_size, max_context_len, shared_blocks,
-                              q_dtype, kv_dtype, &plan, &splits, &ws);
+  const int st = cascade_plan(current_variant(), B, H_Q, H_KV, d_h, block_size,
+                              max_context_len, shared_blocks, q_dtype, kv_dtype, &plan, &splits,
+                              &ws);
   if (st != PKV_OK) return st;
   if (splits_out) *splits_out = splits;
   if (workspace_bytes) *workspace_bytes = ws;
@@ -692,8 +729,8 @@ int pkv_decode_step_cascade(const void* k_new, const void* v_new, float* out, co
   Plan plan;
   int splits = 0;
   size_t ws = 0;
-  st = cascade_plan(B, H_Q, H_KV, d_h, block_size, max_context_len, shared_blocks, q_dtype,
-                    kv_dtype, &plan, &splits, &ws);
+  st = cascade_plan(current_variant(), B, H_Q, H_KV, d_h, block_size, max_context_len,
+                    shared_blocks, q_dtype, kv_dtype, &plan, &splits, &ws);
   if (st != PKV_OK) return st;
   if (!workspace || workspace_bytes < ws) return PKV_ERR_WORKSPACE;
   if (reinterpret_cast<uintptr_t>(workspace) & 15) return PKV_ERR_INVALID_ARG;

@@ -230,24 +230,22 @@ def test_alloc_n_matches_oracle():
 def test_table_row_wider_than_int32_positions_is_rejected():
     # Positions are int32, so a table row may span at most INT32_MAX of them
     # (max_blocks_per_seq * block_size); the check runs on the host before
-    # anything is launched.  The pointers are placeholders: the test runs only
-    # where no device is present, so no call here can reach a device.  One
-    # block less passes the checks and then fails at the launch.
+    # anything is launched.  The pointers are placeholders, so only a row that
+    # the host check rejects is passed (nothing can reach a device), and the
+    # test runs only where no device is present in any case.
     torch = pytest.importorskip("torch")
     if torch.cuda.device_count() > 0:
         pytest.skip("placeholder pointers: runs only where no device is present")
     lib = pkv.load()
     p = C.c_void_p(1 << 12)
     wide = (1 << 31) // 16  # 2^27 blocks of 16 positions = 2^31 positions
-    for mbps, want in ((wide, "invalid_arg"), (wide - 1, "hip")):
-        st = lib.pkv_kv_append(p, p, pkv.PKV_BF16, p, p, pkv.PKV_BF16, None, None, p, mbps, p,
-                               4, 8, 128, 16, 100, None)
-        assert pkv._lib.STATUS_NAMES[st] == want
-        st = lib.pkv_paged_decode_attention(p, p, pkv.PKV_BF16, p, p, pkv.PKV_BF16, None, None,
-                                            p, mbps, p, 16, 4, 32, 8, 128, 16, 100,
-                                            C.c_float(0.1), 0, None, 0, None)
-        assert pkv._lib.STATUS_NAMES[st] in ((want,) if want == "invalid_arg"
-                                             else ("hip", "workspace"))
+    st = lib.pkv_kv_append(p, p, pkv.PKV_BF16, p, p, pkv.PKV_BF16, None, None, p, wide, p,
+                           4, 8, 128, 16, 100, None)
+    assert pkv._lib.STATUS_NAMES[st] == "invalid_arg"
+    st = lib.pkv_paged_decode_attention(p, p, pkv.PKV_BF16, p, p, pkv.PKV_BF16, None, None,
+                                        p, wide, p, 16, 4, 32, 8, 128, 16, 100,
+                                        C.c_float(0.1), 0, None, 0, None)
+    assert pkv._lib.STATUS_NAMES[st] == "invalid_arg"
 
 
 def test_decode_variant_selector():
@@ -270,5 +268,34 @@ def test_decode_variant_selector():
         for t in ts:
             t.join()
         assert len(seen) == 8000 and set(seen) <= {0, 1, 2, 3}
+    finally:
+        pkv.set_decode_variant(prev)
+
+
+def test_decode_workspace_size_covers_every_variant():
+    # pkv_decode_workspace_size is the largest workspace any variant needs, so
+    # it does not depend on the process-wide setting, and it covers the plan
+    # of each variant (host-only calls: nothing is launched)
+    shapes = [(32, 32, 8, 128, 16, 4097, 0, pkv.PKV_BF16, pkv.PKV_BF16),
+              (8, 32, 8, 128, 16, 32768, 0, pkv.PKV_BF16, pkv.PKV_BF16),
+              (128, 32, 1, 128, 16, 16385, 0, pkv.PKV_BF16, pkv.PKV_FP8_E4M3),
+              (3, 4, 2, 8, 4, 34, 8, pkv.PKV_F32, pkv.PKV_F32),
+              (9000, 8, 2, 128, 16, 300, 0, pkv.PKV_BF16, pkv.PKV_BF16)]
+    prev = pkv.set_decode_variant(pkv.PKV_VARIANT_AUTO)
+    try:
+        for shape in shapes:
+            sizes, plans = set(), []
+            for v in (0, 1, 2, 3):
+                pkv.set_decode_variant(v)
+                sizes.add(pkv.decode_workspace_size(*shape))
+                try:
+                    plans.append(pkv.decode_plan(*shape)[2])
+                except pkv.PkvError as e:
+                    assert e.name == "unsupported"
+            assert len(sizes) == 1, shape
+            assert plans and max(plans) == sizes.pop(), shape
+        with pytest.raises(pkv.PkvError) as e:
+            pkv.decode_workspace_size(4, 6, 4, 128, 16, 100)   # H_Q % H_KV != 0
+        assert e.value.name == "invalid_arg"
     finally:
         pkv.set_decode_variant(prev)

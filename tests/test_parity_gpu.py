@@ -630,3 +630,73 @@ def test_invalid_arguments_are_rejected():
         pkv.kv_append(g(w.k_new[0]), g(w.v_new[0]), kc.view(torch.uint8)[..., :128].contiguous(),
                       vc.view(torch.uint8)[..., :128].contiguous(), bt, cl)
     torch.cuda.synchronize()
+
+
+def test_decode_step_with_too_small_workspace_launches_nothing():
+    # the append of a decode step (here the separate append kernel: fp8) must
+    # not run when the attention call would refuse the workspace
+    w = make_workload("fp8_gqa", lens_after=[40, 900, 17])
+    g = lambda t: t.to(DEV).contiguous()
+    kc, vc = g(w.k_cache[0]), g(w.v_cache[0])
+    k0, v0 = kc.clone(), vc.clone()
+    out = torch.empty((w.B, w.H_Q, w.d_h), device=DEV)
+    with pytest.raises(pkv.PkvError) as e:
+        pkv.decode_step(g(w.k_new[0]), g(w.v_new[0]), out, g(w.q[0]), kc, vc, g(w.block_table),
+                        g(w.context_lens), w.max_context_len, w.softmax_scale,
+                        g(w.k_scale[0]), g(w.v_scale[0]), partition_tokens=256,
+                        workspace=torch.empty(256, dtype=torch.uint8, device=DEV))
+    assert e.value.name == "workspace"
+    torch.cuda.synchronize()
+    assert torch.equal(kc, k0) and torch.equal(vc, v0)
+
+
+# ---------------------------------------------------------------------------
+# the kernel variant is read once per call
+# ---------------------------------------------------------------------------
+
+def test_variant_switching_during_calls_keeps_every_result():
+    # a thread switches the process-wide variant between the balanced split
+    # and fixed partitions while attention and decode-step calls run; each
+    # call plans, launches and combines with the one value it read, so every
+    # output still matches the oracle (a workspace of
+    # pkv_decode_workspace_size serves both variants)
+    import threading
+    w = make_workload("llama8b", lens_after=[40, 700, 2049, 300, 17, 1500], H_Q=16, H_KV=4)
+    d = _np(w)
+    _, _, ref = oracle_step(w, d)
+    g = lambda t: t.to(DEV).contiguous()
+    kc, vc, bt, cl = g(w.k_cache[0]), g(w.v_cache[0]), g(w.block_table), g(w.context_lens)
+    kn, vn, q = g(w.k_new[0]), g(w.v_new[0]), g(w.q[0])
+    pkv.kv_append(kn, vn, kc, vc, bt, cl)
+    ws = pkv.decode_workspace_size(w.B, w.H_Q, w.H_KV, w.d_h, w.block_size, w.max_context_len,
+                                   0, pkv.PKV_BF16, pkv.PKV_BF16)
+    work = torch.empty(ws, dtype=torch.uint8, device=DEV)
+    out = torch.empty((w.B, w.H_Q, w.d_h), dtype=torch.float32, device=DEV)
+    stop = threading.Event()
+
+    def flip():
+        while not stop.is_set():
+            pkv.set_decode_variant(pkv.PKV_VARIANT_MFMA)
+            pkv.set_decode_variant(pkv.PKV_VARIANT_MFMA_PARTITION)
+
+    prev = pkv.set_decode_variant(pkv.PKV_VARIANT_AUTO)
+    t = threading.Thread(target=flip)
+    t.start()
+    try:
+        for i in range(60):
+            out.fill_(float("nan"))
+            if i % 2:
+                # the append writes the same row every time (a bit copy)
+                pkv.decode_step(kn, vn, out, q, kc, vc, bt, cl, w.max_context_len,
+                                w.softmax_scale, workspace=work)
+            else:
+                pkv.paged_decode_attention(out, q, kc, vc, bt, cl, w.max_context_len,
+                                           w.softmax_scale, workspace=work)
+            torch.cuda.synchronize()
+            e = _err(out.cpu().numpy().astype(np.float64), ref)
+            assert e <= TOL, (i, e)
+    finally:
+        stop.set()
+        t.join()
+        pkv.set_decode_variant(prev)
+    _log(f"variant switching: 60 calls within {TOL}")
