@@ -329,6 +329,29 @@ int pkv_decode_step(const void* k_new, const void* v_new, float* out, const void
                     float softmax_scale, int32_t partition_tokens, void* workspace,
                     size_t workspace_bytes, pkv_stream_t stream);
 
+/* pkv_decode_step without a caller workspace, for callers that cannot
+ * allocate device memory (code under stream capture, tight serving loops,
+ * hosts that forbid allocation).  Same arguments and results as
+ * pkv_decode_step minus workspace / workspace_bytes: the partial results go
+ * to a static device array of PKV_NOALLOC_SCRATCH_BYTES that the library
+ * holds on every GPU it runs on until the process ends; the call itself
+ * allocates nothing.  Shapes whose workspace (pkv_decode_plan) exceeds that
+ * size are refused with PKV_ERR_WORKSPACE before anything is launched.
+ * Every call on one GPU uses that GPU's one array: calls that overlap in
+ * time on one GPU (other streams, other threads) race on it, and the caller
+ * must order them.  Nothing in the array has to start at any value (each
+ * step writes the partial results and the header it reads back).
+ * PKV_ERR_HIP if the array's device address cannot be obtained. */
+#define PKV_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int pkv_decode_step_noalloc(const void* k_new, const void* v_new, float* out, const void* q,
+                            int q_dtype, void* k_cache, void* v_cache, int kv_dtype,
+                            const float* k_scale, const float* v_scale,
+                            const int32_t* block_table, int32_t max_blocks_per_seq,
+                            const int32_t* context_lens, int32_t max_context_len, int32_t B,
+                            int32_t H_Q, int32_t H_KV, int32_t d_h, int32_t block_size,
+                            int32_t num_blocks, float softmax_scale, int32_t partition_tokens,
+                            pkv_stream_t stream);
+
 /* Cascade decode step over a shared prefix (page 3 "xf_kv_cache",
  * "End-to-end flow": many requests map the same prefix blocks; page 1
  * section 21.5 step 3).  Contract: the first shared_blocks entries of every

@@ -15,7 +15,7 @@ from . import _lib
 from ._lib import (PKV_BF16, PKV_F32, PKV_FP8_E4M3, PKV_VARIANT_AUTO, PKV_VARIANT_GENERIC,
                    PKV_VARIANT_MFMA, PKV_VARIANT_MFMA_PARTITION, PkvError, check, load)
 
-__all__ = ["kv_append", "copy_blocks", "decode_plan", "decode_workspace_size", "paged_decode_attention", "decode_partitions",
+__all__ = ["kv_append", "copy_blocks", "decode_plan", "decode_workspace_size", "decode_step_noalloc", "paged_decode_attention", "decode_partitions",
            "combine_partitions", "set_decode_variant", "BlockPool", "PkvError", "load",
            "prefix_root", "block_hashes", "DIGEST_BYTES", "kv_append_chunk",
            "paged_chunk_attention", "swap_record_bytes", "swap_out", "swap_in", "decode_step",
@@ -216,6 +216,19 @@ def decode_step(k_new, v_new, out, q, k_cache, v_cache, block_table, context_len
     check(load().pkv_decode_step(_ptr(k_new), _ptr(v_new), *_attn_args(
         out, q, k_cache, v_cache, block_table, context_lens, max_context_len, softmax_scale,
         k_scale, v_scale, partition_tokens, workspace, stream)), "pkv_decode_step")
+
+
+def decode_step_noalloc(k_new, v_new, out, q, k_cache, v_cache, block_table, context_lens,
+                        max_context_len, softmax_scale, k_scale=None, v_scale=None,
+                        partition_tokens=0, stream=None):
+    """pkv_decode_step_noalloc: pkv_decode_step with the library's static
+    device workspace (no caller workspace, nothing allocated)."""
+    args = _attn_args(out, q, k_cache, v_cache, block_table, context_lens, max_context_len,
+                      softmax_scale, k_scale, v_scale, partition_tokens, None, stream)
+    # drop the workspace pointer and size of the plain step's argument list
+    args = args[:-3] + args[-1:]
+    check(load().pkv_decode_step_noalloc(_ptr(k_new), _ptr(v_new), *args),
+          "pkv_decode_step_noalloc")
 
 
 def cascade_plan(B, H_Q, H_KV, d_h, block_size, max_context_len, shared_blocks,

@@ -66,6 +66,9 @@ SIGNATURES = {
     "pkv_decode_step": (C.c_int, [_vp, _vp, _vp, _vp, C.c_int, _vp, _vp, C.c_int, _vp, _vp, _vp,
                                   _i32, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f, _i32,
                                   _vp, _sz, _vp]),
+    "pkv_decode_step_noalloc": (C.c_int, [_vp, _vp, _vp, _vp, C.c_int, _vp, _vp, C.c_int, _vp,
+                                          _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32,
+                                          _i32, _i32, _f, _i32, _vp]),
     "pkv_cascade_plan": (C.c_int, [_i32, _i32, _i32, _i32, _i32, _i32, _i32, C.c_int, C.c_int,
                                    _pi32, C.POINTER(_sz)]),
     "pkv_decode_step_cascade": (C.c_int, [_vp, _vp, _vp, _vp, C.c_int, _vp, _vp, C.c_int, _vp,

@@ -18,7 +18,7 @@ LIB = os.path.join(PKG, "libpkv.so")
 BENCH_LIB = os.path.join(PKG, "libpkv_bench.so")   # measurement helper of bench.py
 
 HIP_SOURCES = ["kv_append.hip", "copy_blocks.hip", "decode_generic.hip", "decode_mfma.hip",
-               "combine.hip", "chunk_attention.hip", "swap.hip"]
+               "combine.hip", "chunk_attention.hip", "swap.hip", "noalloc.hip"]
 CXX_SOURCES = ["api.cpp", "pool.cpp", "sha256.cpp"]
 
 FLAGS = [

@@ -1,0 +1,108 @@
+"""The decode step without a caller workspace (pkv_decode_step_noalloc),
+called through the C ABI.
+
+On the GPU: two calls in a row, the second with a smaller batch, each
+compared with pkv_decode_step given a workspace of its own: pools and
+outputs must be bitwise equal (the same kernels and split run on the same
+inputs; only where the partial results live differs), and the outputs
+within 2e-3 of the float64 oracle.  The static array keeps the previous
+call's partial results, so the second call also shows that nothing in it
+has to start cleared.  On the host: shapes whose workspace exceeds the
+array are refused before any device call.
+"""
+
+import ctypes as C
+
+import numpy as np
+import pytest
+import torch
+
+import paged_kv_cache_105_amd as pkv
+from oracle import paged
+from paged_kv_cache_105_amd.workloads import as_numpy, make_workload
+
+DEV = torch.device("cuda:0")
+TOL = 2e-3
+
+
+def _inputs(w):
+    g = lambda t: t.to(DEV).contiguous()
+    d = dict(q=g(w.q[0]), kn=g(w.k_new[0]), vn=g(w.v_new[0]), kc=g(w.k_cache[0]),
+             vc=g(w.v_cache[0]), bt=g(w.block_table), cl=g(w.context_lens),
+             ks=g(w.k_scale[0]) if w.k_scale else None,
+             vs=g(w.v_scale[0]) if w.v_scale else None)
+    return d
+
+
+def _step(w, d, noalloc):
+    kc, vc = d["kc"].clone(), d["vc"].clone()
+    out = torch.full((w.B, w.H_Q, w.d_h), float("nan"), dtype=torch.float32, device=DEV)
+    if noalloc:
+        pkv.decode_step_noalloc(d["kn"], d["vn"], out, d["q"], kc, vc, d["bt"], d["cl"],
+                                w.max_context_len, w.softmax_scale, d["ks"], d["vs"])
+    else:
+        ws = pkv.decode_workspace_size(w.B, w.H_Q, w.H_KV, w.d_h, w.block_size,
+                                       w.max_context_len, 0, pkv.dtype_code(w.q[0]),
+                                       pkv.dtype_code(w.k_cache[0]))
+        work = torch.empty(max(ws, 256), dtype=torch.uint8, device=DEV)
+        pkv.decode_step(d["kn"], d["vn"], out, d["q"], kc, vc, d["bt"], d["cl"],
+                        w.max_context_len, w.softmax_scale, d["ks"], d["vs"], workspace=work)
+    torch.cuda.synchronize()
+    return kc.cpu(), vc.cpu(), out.cpu().numpy().astype(np.float64)
+
+
+def _oracle(w, requests):
+    a = lambda t: as_numpy(t)
+    return paged.decode_step(a(w.q[0]), w.q_dtype, a(w.k_new[0]), a(w.v_new[0]),
+                             a(w.k_cache[0]).copy(), a(w.v_cache[0]).copy(), w.kv_dtype,
+                             a(w.block_table), a(w.context_lens), w.block_size,
+                             w.softmax_scale, a(w.k_scale[0]) if w.k_scale else None,
+                             a(w.v_scale[0]) if w.v_scale else None, requests=requests,
+                             inplace=True)[2]
+
+
+# first call, then a smaller second one: the bench's 8B-style batch (append
+# fused into the attention launch), and fp8 with 32 query heads per KV head
+# (separate append kernel, two head groups per wave)
+PAIRS = {
+    "bf16": [("llama8b", {}), ("llama8b", dict(lens_after=[40, 700, 17], H_Q=8, H_KV=2))],
+    "fp8": [("fp8_mqa", dict(B=24)), ("fp8_mqa", dict(lens_after=[1, 16, 300, 2049]))],
+}
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("pair", list(PAIRS), ids=list(PAIRS))
+def test_noalloc_step_equals_decode_step_on_two_calls(pair):
+    for call, (name, kw) in enumerate(PAIRS[pair]):
+        w = make_workload(name, **kw)
+        print(f"noalloc {pair} call {call}: {name} B={w.B} max_len={w.max_context_len}",
+              flush=True)
+        d = _inputs(w)
+        kc_a, vc_a, out_a = _step(w, d, noalloc=False)
+        kc_b, vc_b, out_b = _step(w, d, noalloc=True)
+        assert torch.equal(kc_a, kc_b) and torch.equal(vc_a, vc_b), (pair, call)
+        assert np.all(np.isfinite(out_b))
+        assert np.array_equal(out_a, out_b), (pair, call)
+        requests = list(range(0, w.B, max(1, w.B // 6)))
+        ref = _oracle(w, requests)
+        err = float(np.max(np.abs(out_b[requests] - ref[requests])))
+        assert err <= TOL, (pair, call, err)
+
+
+def test_noalloc_refuses_shapes_beyond_the_array():
+    # fixed partitions of 16 positions for 64 requests x 64 query heads at
+    # 16,384 positions need 64 x 64 x 1024 x 130 x 4 bytes (~2.2 GB) of
+    # partial results: refused with WORKSPACE before any device call.  The
+    # pointers are placeholders, so this runs only where no device is present.
+    if torch.cuda.device_count() > 0:
+        pytest.skip("placeholder pointers: runs only where no device is present")
+    lib = pkv.load()
+    p = C.c_void_p(1 << 12)
+    prev = pkv.set_decode_variant(pkv.PKV_VARIANT_MFMA_PARTITION)
+    try:
+        st = lib.pkv_decode_step_noalloc(p, p, p, p, pkv.PKV_BF16, p, p, pkv.PKV_BF16, None,
+                                         None, p, 1024, p, 16384, 64, 64, 8, 128, 16, 100000,
+                                         C.c_float(0.1), 16, None)
+    finally:
+        pkv.set_decode_variant(prev)
+    assert pkv._lib.STATUS_NAMES[st] == "workspace"
