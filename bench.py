@@ -13,7 +13,9 @@ Prints ONE JSON line on stdout (diagnostics go to stderr).  ``value`` is the
 achieved algorithmic GB/s of the whole step; ``roofline`` reports the
 partition kernel alone, timed with HIP events on the stream it runs on;
 ``cpu_baseline`` times the float64 CPU oracle on a bounded sample of the
-same workload.
+same workload, on one core and (``all_cores``) on every allowed core;
+``also_measured`` holds the step and kernel figures of the other target
+workloads (``--also``, by default the 32K-context batch) from the same run.
 """
 
 from __future__ import annotations
@@ -205,45 +207,113 @@ def swap_measurement(w, pool, k_scale, v_scale, stream, dev, reps: int = 5):
     return res
 
 
-def cpu_baseline(w, layer_tensors, budget_s: float):
-    """Time the oracle (as it stands) on a bounded sample: the append of the
-    whole batch, then attention request by request until ~budget_s."""
+# ---- CPU oracle baselines ---------------------------------------------------
+#
+# They run before this process touches the GPU: the all-cores figure forks
+# worker processes, which is only safe while no device has been opened.  The
+# inputs are drawn on the host with the same recipe (lengths and block tables
+# are identical; values come from the host generator).
+
+_CPU_DATA = None
+
+
+def _cpu_workload(name: str):
     import numpy as np
+
+    from paged_kv_cache_105_amd.workloads import as_numpy, make_workload
+    w = make_workload(name, layers=1) if name == "shared_prefix" else make_workload(name)
+    d = dict(q=as_numpy(w.q[0]), kn=as_numpy(w.k_new[0]), vn=as_numpy(w.v_new[0]),
+             kc=as_numpy(w.k_cache[0]).copy(), vc=as_numpy(w.v_cache[0]).copy(),
+             table=as_numpy(w.block_table), lens=as_numpy(w.context_lens),
+             ks=as_numpy(w.k_scale[0]) if w.k_scale else None,
+             vs=as_numpy(w.v_scale[0]) if w.v_scale else None)
+    np.ones((2, 2)) @ np.ones((2, 2))   # load BLAS, so that its thread limit applies
+    return w, d
+
+
+def _attend_request(w, d, b):
+    from oracle import paged
+    from paged_kv_cache_105_amd import metrics
+    paged.attend(d["q"], w.q_dtype, d["kc"], d["vc"], w.kv_dtype, d["table"], d["lens"],
+                 w.block_size, w.softmax_scale, d["ks"], d["vs"], requests=[b])
+    return metrics.attention_bytes([int(d["lens"][b])], w.H_Q, w.H_KV, w.d_h, w.block_size,
+                                   w.kv_dtype, w.q_dtype)["total"]
+
+
+def _cpu_worker(args):
+    """One worker of the all-cores run: its share of the requests (b = k,
+    k + n, ...), over and over, until the deadline; BLAS on one thread."""
+    k, n, deadline = args
+    from threadpoolctl import threadpool_limits
+    w, d = _CPU_DATA
+    nbytes, reqs = 0, 0
+    with threadpool_limits(limits=1):
+        while time.time() < deadline:
+            for b in range(k, w.B, n):
+                nbytes += _attend_request(w, d, b)
+                reqs += 1
+                if time.time() >= deadline:
+                    break
+    return nbytes, reqs
+
+
+def cpu_baselines(name: str, budget_1: float, budget_n: float):
+    """The oracle as it stands, on a bounded sample of the workload:
+    one core (BLAS pinned to one thread): whole decode steps -- the append of
+    the batch, then attention request by request -- until ~budget_1 s;
+    all allowed cores: one process per core, each attending its share of the
+    requests with BLAS on one thread, for ~budget_n s of wall time (the
+    append is serial and tiny, so the sample is attention only)."""
+    import multiprocessing as mp
+
     from threadpoolctl import threadpool_limits
 
     from oracle import paged
     from paged_kv_cache_105_amd import metrics
-    from paged_kv_cache_105_amd.workloads import as_numpy
+    global _CPU_DATA
+    t_gen = time.perf_counter()
+    w, d = _cpu_workload(name)
+    log(f"cpu baseline inputs drawn on the host in {time.perf_counter() - t_gen:.1f} s")
 
-    q, kn, vn, kc, vc, ks, vs = layer_tensors
-    d = dict(q=as_numpy(q), kn=as_numpy(kn), vn=as_numpy(vn), kc=as_numpy(kc).copy(),
-             vc=as_numpy(vc).copy(), table=as_numpy(w.block_table), lens=as_numpy(w.context_lens),
-             ks=None if ks is None else as_numpy(ks), vs=None if vs is None else as_numpy(vs))
-    # whole decode steps (append of the batch, then attention request by
-    # request) until the time budget is spent; a partial last pass counts
-    # only the requests it finished
     nbytes, passes, reqs = 0, 0, 0
     with threadpool_limits(limits=1):
         t0 = time.perf_counter()
-        while time.perf_counter() - t0 < budget_s:
+        while time.perf_counter() - t0 < budget_1:
             paged.append(d["kc"], d["vc"], w.kv_dtype, d["kn"], d["vn"], w.q_dtype, d["table"],
                          d["lens"], w.block_size, d["ks"], d["vs"], inplace=True)
             nbytes += metrics.append_bytes(w.B, w.H_KV, w.d_h, w.kv_dtype, w.q_dtype)
             for b in range(w.B):
-                paged.attend(d["q"], w.q_dtype, d["kc"], d["vc"], w.kv_dtype, d["table"],
-                             d["lens"], w.block_size, w.softmax_scale, d["ks"], d["vs"],
-                             requests=[b])
-                nbytes += metrics.attention_bytes([int(d["lens"][b])], w.H_Q, w.H_KV, w.d_h,
-                                                  w.block_size, w.kv_dtype, w.q_dtype)["total"]
+                nbytes += _attend_request(w, d, b)
                 reqs += 1
-                if time.perf_counter() - t0 > budget_s:
+                if time.perf_counter() - t0 > budget_1:
                     break
             passes += 1
         dt = time.perf_counter() - t0
-    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"one layer of this workload: {passes} decode step(s) (append of all "
-                      f"{w.B} requests, attention of {reqs} request-steps), float64 numpy, "
-                      f"BLAS pinned to 1 thread, {dt:.1f} s"}
+    one = {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+           "sample": f"one layer of {name}: {passes} decode step(s) (append of all {w.B} "
+                     f"requests, attention of {reqs} request-steps), float64 numpy, BLAS "
+                     f"pinned to 1 thread, {dt:.1f} s"}
+
+    allowed = len(os.sched_getaffinity(0))
+    # the box's share of host cores (OMP_NUM_THREADS there) caps the workers
+    cap = int(os.environ.get("OMP_NUM_THREADS", "0") or 0)
+    n = min(allowed, cap) if cap > 0 else allowed
+    _CPU_DATA = (w, d)
+    deadline = time.time() + budget_n
+    t0 = time.perf_counter()
+    with mp.get_context("fork").Pool(n) as pool:
+        res = pool.map(_cpu_worker, [(k, n, deadline) for k in range(n)])
+    dt = time.perf_counter() - t0
+    _CPU_DATA = None
+    nb = sum(r[0] for r in res)
+    rq = sum(r[1] for r in res)
+    alln = {"value": round(nb / dt / 1e9, 4), "unit": "GB/s", "cores": n,
+            "cores_allowed": allowed, "kind": "oracle",
+            "sample": f"one layer of {name}: attention of {rq} request-steps by {n} worker "
+                      f"processes (one per core, requests dealt round robin), float64 numpy, "
+                      f"BLAS on 1 thread each, {dt:.1f} s wall"}
+    log(f"cpu oracle, 1 core: {one['value']} GB/s; {n} cores: {alln['value']} GB/s")
+    return one, alln
 
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, vendor figure
@@ -275,6 +345,7 @@ def chunk_cpu_baseline(name: str, budget_s: float):
     lens, qs = w.context_lens.tolist(), w.query_start.tolist()
     flops = chunk_flops(lens, qs, w.H_Q, w.d_h)
     d = [as_numpy(t[0]) for t in (w.q, w.k_new, w.v_new, w.k_cache, w.v_cache)]
+    np.ones((2, 2)) @ np.ones((2, 2))   # load BLAS, so that its thread limit applies
     runs, t0 = 0, time.perf_counter()
     with threadpool_limits(limits=1):
         while True:
@@ -379,50 +450,25 @@ def chunk_main(args, w, dev):
     print(json.dumps(res), flush=True)
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="llama8b")
-    ap.add_argument("--partition", type=int, default=0, help="positions per partition, 0 = default")
-    ap.add_argument("--rotate", type=int, default=4, help="KV pool copies for cold-cache timing")
-    ap.add_argument("--variant", type=int, default=0, help="0 auto, 1 generic, 2 mfma")
-    ap.add_argument("--cpu-budget", type=float, default=12.0)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--copy-blocks", type=int, default=0, metavar="N",
-                    help="also time pkv_copy_blocks on N random disjoint block pairs")
-    ap.add_argument("--no-cascade", action="store_true",
-                    help="plain decode steps even where requests share prefix blocks")
-    ap.add_argument("--no-swap", action="store_true",
-                    help="skip the swap-to-host measurement")
-    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
-                    help="after the bench, copy a MIB-sized buffer 5 times (plain copy kernel "
-                         "of known size, to scale HBM counters)")
-    args = ap.parse_args()
-
-    if args.gpus != 1:
-        log(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported")
-        sys.exit(2)
-
+def decode_measure(args, name, dev, full=True):
+    """Measure one decode workload: the step (append + attention + combine)
+    by wall clock over args.steps steps, and the partition kernel alone by
+    HIP events around back-to-back launches on its stream.  With ``full``,
+    also the reference bandwidths of plain kernels on this machine, the
+    compute-free gather of the same tiles, and the optional block-copy and
+    calibration measurements.  Returns (record, workload, pools)."""
     import torch
 
     import paged_kv_cache_105_amd as pkv
     from paged_kv_cache_105_amd import metrics
     from paged_kv_cache_105_amd.workloads import make_workload
 
-    pkv.load()
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
     t_gen = time.perf_counter()
-    w = make_workload(args.workload, device=dev)
+    w = make_workload(name, device=dev)
     lens = w.context_lens.cpu().tolist()
-    log(f"workload {args.workload}: B={w.B} H_Q={w.H_Q} H_KV={w.H_KV} d_h={w.d_h} "
+    log(f"workload {name}: B={w.B} H_Q={w.H_Q} H_KV={w.H_KV} d_h={w.d_h} "
         f"bs={w.block_size} kv={w.kv_dtype} layers={w.layers} blocks={w.num_blocks} "
         f"max_len={w.max_context_len} (generated in {time.perf_counter() - t_gen:.1f} s)")
-    if w.max_q_len > 1:
-        chunk_main(args, w, dev)
-        return
 
     # pools per (rotation, layer)
     R = max(1, args.rotate) if w.layers == 1 else 1
@@ -501,12 +547,32 @@ def main():
     step_bytes = w.layers * (att["total"] + app)
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
     achieved = att["total"] / (kern_avg_ms * 1e-3) / 1e9
-    traffic = measured_traffic(args.workload, pt)
+    traffic = measured_traffic(name, pt)
     log(f"partition={pt} parts={parts} workspace={ws_bytes} B; step {ms_per_step * 1e3:.1f} us "
-        f"({ms_per_step * 1e3 / w.layers:.1f} us/layer); partition kernel avg "
+        f"({ms_per_step * 1e3 / w.layers:.1f} us/layer) = {value:.0f} GB/s = "
+        f"{100 * value / PEAK_GBS:.1f}% of peak; partition kernel avg "
         f"{kern_avg_ms * 1e3:.1f} us (batches: {', '.join(f'{x * 1e3:.1f}' for x in kern_ms)}); "
         f"KV bytes/layer {att['kv']}; kernel {achieved:.0f} GB/s = "
         f"{100 * achieved / PEAK_GBS:.1f}% of peak")
+    kernel = {0: "decode_mfma_flat_kernel", 1: "decode_generic_kernel",
+              2: "decode_mfma_flat_kernel", 3: "decode_mfma_kernel"}[args.variant]
+    rec = {"value": round(value, 2), "ms_per_step": round(ms_per_step, 5),
+           "config": {"workload": name, "B": w.B, "H_Q": w.H_Q, "H_KV": w.H_KV,
+                      "d_h": w.d_h, "block_size": w.block_size, "kv_dtype": w.kv_dtype,
+                      "q_dtype": w.q_dtype, "layers": w.layers, "partition_tokens": pt,
+                      "partitions_max": parts, "pool_copies": R,
+                      "cascade_shared_blocks": w.shared_blocks if cascade else 0,
+                      "mean_context": round(sum(lens) / len(lens), 1),
+                      "us_per_step_per_layer": round(ms_per_step * 1e3 / w.layers, 2),
+                      "pct_of_peak_step": round(100 * value / PEAK_GBS, 2)},
+           "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_GBS,
+                        "unit": "GB/s", "frac": round(achieved / PEAK_GBS, 4),
+                        "traffic": traffic, "kernel": kernel,
+                        "algorithmic_bytes_per_launch": att["total"],
+                        "avg_launch_us": round(kern_avg_ms * 1e3, 3)},
+           "dtype": w.kv_dtype}
+    if not full:
+        return rec, w, pools
 
     # reference bandwidths of plain torch kernels on this machine (context for the
     # % of peak): a 1 GiB device-to-device copy and a 2 GiB read-only sum
@@ -557,9 +623,6 @@ def main():
         log(f"copy_blocks: {n} pairs x {blk} B x (K, V) in {cms * 1e3:.1f} us = "
             f"{ref['copy_blocks_gbs']} GB/s read+write")
 
-    swap = swap_measurement(w, pools[0][0], ks[0], vs[0], stream, dev) if not args.no_swap \
-        else None
-
     if args.calibrate_copy > 0:
         src = torch.ones(args.calibrate_copy * 2 ** 20 // 4, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
@@ -568,45 +631,116 @@ def main():
         torch.cuda.synchronize()
         log(f"calibration copy: {args.calibrate_copy} MiB read + written, 5 launches")
 
+    rec["config"]["reference_gbs"] = ref
+    rec["config"]["pct_of_gather_reference"] = round(100 * achieved / ref["gather_gbs"], 1)
+    return rec, w, pools
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="llama8b")
+    ap.add_argument("--also", default="long32k",
+                    help="comma-separated decode workloads measured in the same run as "
+                         "sub-records (step and kernel figures); empty for none")
+    ap.add_argument("--partition", type=int, default=0, help="positions per partition, 0 = default")
+    ap.add_argument("--rotate", type=int, default=4, help="KV pool copies for cold-cache timing")
+    ap.add_argument("--variant", type=int, default=0, help="0 auto, 1 generic, 2 mfma")
+    ap.add_argument("--cpu-budget", type=float, default=10.0,
+                    help="seconds of the one-core oracle sample")
+    ap.add_argument("--cpu-budget-all", type=float, default=6.0,
+                    help="wall seconds of the all-cores oracle sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-blocks", type=int, default=0, metavar="N",
+                    help="also time pkv_copy_blocks on N random disjoint block pairs")
+    ap.add_argument("--no-cascade", action="store_true",
+                    help="plain decode steps even where requests share prefix blocks")
+    ap.add_argument("--no-swap", action="store_true",
+                    help="skip the swap-to-host measurement")
+    ap.add_argument("--no-host", action="store_true",
+                    help="skip the host prefix-identity measurement")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="after the bench, copy a MIB-sized buffer 5 times (plain copy kernel "
+                         "of known size, to scale HBM counters)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        log(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported")
+        sys.exit(2)
+
+    from paged_kv_cache_105_amd.workloads import CONFIGS
+    chunk = CONFIGS[args.workload].get("lens") in ("fixed_after", "prefix_chunk")
+
+    # the CPU oracle first: its all-cores run forks, before any device use
     cpu = None
-    if not args.no_cpu_baseline:
-        cpu = cpu_baseline(w, (w.q[0], w.k_new[0], w.v_new[0], w.k_cache[0], w.v_cache[0],
-                               ks[0], vs[0]), args.cpu_budget)
-        log(f"cpu oracle: {cpu}")
+    if not args.no_cpu_baseline and not chunk:
+        one, alln = cpu_baselines(args.workload, args.cpu_budget, args.cpu_budget_all)
+        cpu = dict(one)
+        cpu["all_cores"] = alln
+
+    import torch
+
+    import paged_kv_cache_105_amd as pkv
+    from paged_kv_cache_105_amd.workloads import make_workload
+
+    pkv.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    if chunk:
+        w = make_workload(args.workload, device=dev)
+        log(f"workload {args.workload}: B={w.B} H_Q={w.H_Q} H_KV={w.H_KV} d_h={w.d_h} "
+            f"bs={w.block_size} kv={w.kv_dtype} new tokens={w.total_q}")
+        chunk_main(args, w, dev)
+        return
+
+    rec, w, pools = decode_measure(args, args.workload, dev, full=True)
+    stream = torch.cuda.current_stream()
+    ks = w.k_scale or [None] * w.layers
+    vs = w.v_scale or [None] * w.layers
+    swap = swap_measurement(w, pools[0][0], ks[0], vs[0], stream, dev) if not args.no_swap \
+        else None
+    del w, pools
+    torch.cuda.empty_cache()
+
+    # the other target workloads, measured in the same run
+    also = {}
+    for name in [x for x in args.also.split(",") if x and x != args.workload]:
+        sub, w2, p2 = decode_measure(args, name, dev, full=False)
+        also[name] = {"us_per_step_per_layer": sub["config"]["us_per_step_per_layer"],
+                      "step_gbs": sub["value"],
+                      "pct_of_peak_step": sub["config"]["pct_of_peak_step"],
+                      "kernel_us": sub["roofline"]["avg_launch_us"],
+                      "kernel_gbs": sub["roofline"]["achieved"],
+                      "kernel_frac": sub["roofline"]["frac"],
+                      "traffic": sub["roofline"]["traffic"],
+                      "algorithmic_bytes_per_launch":
+                          sub["roofline"]["algorithmic_bytes_per_launch"],
+                      "config": {k: sub["config"][k] for k in
+                                 ("B", "H_Q", "H_KV", "d_h", "block_size", "kv_dtype",
+                                  "mean_context", "pool_copies")}}
+        del w2, p2
+        torch.cuda.empty_cache()
 
     res = {
         "metric": METRIC,
-        "value": round(value, 2),
+        "value": rec["value"],
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 5),
+        "ms_per_step": rec["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": w.kv_dtype,
+        "dtype": rec["dtype"],
         "data": "synthetic",
-        "config": {"workload": args.workload, "B": w.B, "H_Q": w.H_Q, "H_KV": w.H_KV,
-                   "d_h": w.d_h, "block_size": w.block_size, "kv_dtype": w.kv_dtype,
-                   "q_dtype": w.q_dtype, "layers": w.layers, "partition_tokens": pt,
-                   "partitions_max": parts, "pool_copies": R,
-                   "cascade_shared_blocks": w.shared_blocks if cascade else 0,
-                   "mean_context": round(sum(lens) / len(lens), 1),
-                   "us_per_step_per_layer": round(ms_per_step * 1e3 / w.layers, 2),
-                   "pct_of_peak_step": round(100 * value / PEAK_GBS, 2),
-                   "reference_gbs": ref,
-                   "pct_of_gather_reference": round(100 * achieved / ref["gather_gbs"], 1)},
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / PEAK_GBS, 4),
-                     "traffic": traffic,
-                     "kernel": {0: "decode_mfma_flat_kernel", 1: "decode_generic_kernel",
-                                2: "decode_mfma_flat_kernel",
-                                3: "decode_mfma_kernel"}[args.variant],
-                     "algorithmic_bytes_per_launch": att["total"],
-                     "avg_launch_us": round(kern_avg_ms * 1e3, 3)},
+        "config": rec["config"],
+        "roofline": rec["roofline"],
         "cpu_baseline": cpu,
-        "host_prefix_identity": host_prefix_identity(w.block_size),
+        "also_measured": also,
+        "host_prefix_identity": None if args.no_host else host_prefix_identity(16),
         "swap_32k_request_layer": swap,
     }
     print(json.dumps(res), flush=True)
