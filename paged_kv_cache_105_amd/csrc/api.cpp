@@ -95,13 +95,13 @@ struct Plan {
 int flat_waves_cached(int kv_dtype, int g, int B, bool cascade = false) {
   // the occupancy query depends on the kernel instance and its LDS size
   static std::mutex mu;
-  static std::map<std::tuple<int, int, int, int>, int> cache;
+  static std::map<std::tuple<int, int, int, int, int>, int> cache;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) {
     (void)hipGetLastError();
     dev = -1;
   }
-  const auto key = std::make_tuple(dev, kv_dtype, (g > 16 ? 2 : 1) + (cascade ? 4 : 0), B);
+  const auto key = std::make_tuple(dev, kv_dtype, g, cascade ? 1 : 0, B);
   std::lock_guard<std::mutex> lock(mu);
   auto it = cache.find(key);
   if (it != cache.end()) return it->second;

@@ -19,6 +19,8 @@
 // request)) and the flat kernel (the balanced split below), which is the
 // one the library picks for batches up to 8192 requests.
 
+#include <cstdlib>
+
 #include "cascade_prefix.h"
 #include "mfma_tiles.h"
 
@@ -159,14 +161,14 @@ __global__ __launch_bounds__(64, 2) void decode_mfma_kernel(DecodeArgs a) {
   }
 }
 
-// Flat mode: the W = gridDim.x waves share the blocks of all (request, KV
-// head) sequences equally.  Sequence (b, h) holds nb_b = ceil(n_b / 16)
+// Flat mode: the W = gridDim.x workgroups share the blocks of all (request,
+// KV head) sequences equally.  Sequence (b, h) holds nb_b = ceil(n_b / 16)
 // blocks and starts at H_KV * P_b + h * nb_b, P_b = sum of nb over requests
 // before b; T = H_KV * P_B blocks in all, cut into C = min(W, T) chunks.
-// Wave w < C takes [floor(w T / C), floor((w + 1) T / C)) and walks the
-// sequences it overlaps: a sequence inside the chunk is written final, a cut
-// one as a partial in slot 0 (the chunk's first sequence) or slot 1 (its
-// last).
+// Workgroup w < C takes [floor(w T / C), floor((w + 1) T / C)) (its waves
+// split it, see below) and walks the sequences it overlaps: a sequence
+// inside the chunk is written final, a cut one as a partial in slot 0 (the
+// chunk's first sequence) or slot 1 (its last).
 //
 // The walk is one stream of loads over the whole chunk.  It moves in groups
 // of up to 64 blocks of one sequence (one table entry per lane); when a group
@@ -261,11 +263,30 @@ __device__ __forceinline__ int load_window(const DecodeArgs& a, const Cursor& c,
   return v;
 }
 
-template <int KV, int NG, bool FUSED, bool CASCADE>
-__global__ __launch_bounds__(64, 2) void decode_mfma_flat_kernel(DecodeArgs a) {
-  __shared__ u32x4 lds_k[kBS * 16];
+// HW waves per workgroup share its chunk [lo, hi): wave k walks
+// [q_k, q_(k+1)), q_k = lo + min(k ceil((hi - lo) / HW), hi - lo), so only
+// the last waves of a short chunk can have nothing to do.  The waves read
+// different blocks, so a SIMD interleaves independent walks, while the
+// chunks -- and so the partial results and the combine -- stay those of one
+// walk per chunk: a sequence cut inside the chunk is merged through LDS at
+// the end.  The lowest wave that covers it (its walk ends in it) keeps it
+// in registers; each later wave covering it leaves its piece in its own LDS
+// slot; after one barrier the first wave merges the run of pieces by the
+// log-sum-exp rule and writes the sequence as one walk over the chunk would
+// have.
+template <int KV, int NG, bool FUSED, bool CASCADE, int HW = 1>
+__global__ __launch_bounds__(64 * HW, 2) void decode_mfma_flat_kernel(DecodeArgs a) {
+  static_assert(HW == 1 || ((HW == 2 || HW == 4) && !CASCADE),
+                "split chunks: two or four waves, no cascade");
+  __shared__ u32x4 lds_k_all[HW][kBS * 16];
+  // the pieces waves 1 .. HW - 1 leave for the merge: [wave - 1][group][o
+  // values, m, l][lane]
+  constexpr int kSlot = NG * 34 * 64;
+  __shared__ float piece_lds[HW > 1 ? (HW - 1) * kSlot : 1];
   extern __shared__ int32_t prefix[];  // [B + 1]
   const LaneMap L = lane_map();
+  const int hw = HW > 1 ? uniform(static_cast<int>(threadIdx.x >> 6)) : 0;
+  u32x4* lds_k = lds_k_all[hw];
   int w = blockIdx.x, W = gridDim.x;
   if constexpr (CASCADE) {
     // the first prefix_waves workgroups score the whole batch against the
@@ -297,18 +318,22 @@ __global__ __launch_bounds__(64, 2) void decode_mfma_flat_kernel(DecodeArgs a) {
       if (L.lane >= off) x += y;
     }
     x += carry;
-    if (b < B) prefix[b + 1] = x;
+    if (hw == 0 && b < B) prefix[b + 1] = x;  // every wave holds the same x
     carry = __builtin_amdgcn_readlane(x, 63);
   }
-  if (L.lane == 0) prefix[0] = 0;
-  lds_wave_sync();
+  if (hw == 0 && L.lane == 0) prefix[0] = 0;
+  if constexpr (HW > 1) {
+    __syncthreads();  // the prefix wave 0 wrote
+  } else {
+    lds_wave_sync();
+  }
   const long long T = static_cast<long long>(HKV) * carry;
   // chunks of at least one block each: with more waves than blocks the
   // surplus waves stay idle (an empty chunk would leave a hole in the
   // sequence of pieces the combine walks)
   const int C = static_cast<int>(T < W ? T : W);
   const FlatLayout FL = flat_layout(B, W, a.g, kD);
-  if (w == 0) {
+  if (w == 0 && hw == 0) {
     if (L.lane == 0) {
       WsHeader* hd = reinterpret_cast<WsHeader*>(a.ws);
       hd->mode = kWsFlat;
@@ -334,15 +359,31 @@ __global__ __launch_bounds__(64, 2) void decode_mfma_flat_kernel(DecodeArgs a) {
     lo = flat_chunk_lo(w, T, C);
     hi = flat_chunk_lo(w + 1, T, C);
   }
+  // this wave's part of the chunk: [wlo, whi) = [q_hw, q_(hw + 1))
+  long long wlo = lo, whi = hi, part = hi - lo;
+  if constexpr (HW > 1) {
+    part = (hi - lo + HW - 1) / HW;
+    wlo = lo + min(hw * part, hi - lo);
+    whi = lo + min((hw + 1) * part, hi - lo);
+  }
+  float* part_o = reinterpret_cast<float*>(a.ws + FL.o);
+  float* part_ml = reinterpret_cast<float*>(a.ws + FL.ml);
+  // a sequence cut inside the chunk, held in this wave's registers until
+  // the merge
+  bool held = false;
+  int held_b = 0, held_h = 0;
+  long long held_S = 0, held_E = 0;
+  Acc<NG> acc;
 
-  // the sequence holding block lo: request = the last b with H_KV * P_b <= lo
+  if (wlo < whi) {
+  // the sequence holding block wlo: request = the last b with H_KV * P_b <= wlo
   Cursor cur;
   {
     int pb, pb1;
     if (B <= 64) {
       // the prefix is still in the lanes (lane l: P_(l+1)): the requests
-      // with H_KV * P_(b) <= lo, b >= 1, are lanes 0 .. count - 1
-      const bool le = L.lane < B && static_cast<long long>(HKV) * x <= lo;
+      // with H_KV * P_(b) <= wlo, b >= 1, are lanes 0 .. count - 1
+      const bool le = L.lane < B && static_cast<long long>(HKV) * x <= wlo;
       const int count = __builtin_popcountll(__ballot(le));
       cur.b = min(count, B - 1);
       pb = cur.b == 0 ? 0 : __builtin_amdgcn_readlane(x, cur.b - 1);
@@ -350,24 +391,21 @@ __global__ __launch_bounds__(64, 2) void decode_mfma_flat_kernel(DecodeArgs a) {
     } else {
       int l0 = 0, l1 = B - 1;
       while (l0 < l1) {
-        const int mid = (l0 + l1 + 1) >> 1;
-        if (static_cast<long long>(HKV) * prefix[mid] <= lo) l0 = mid; else l1 = mid - 1;
+        const int m2 = (l0 + l1 + 1) >> 1;
+        if (static_cast<long long>(HKV) * prefix[m2] <= wlo) l0 = m2; else l1 = m2 - 1;
       }
       cur.b = uniform(l0);
       pb = uniform(prefix[cur.b]);
       pb1 = uniform(prefix[cur.b + 1]);
     }
     cur.nb = pb1 - pb;
-    cur.h = small ? (static_cast<int>(lo) - HKV * pb) / cur.nb
-                  : static_cast<int>((lo - static_cast<long long>(HKV) * pb) / cur.nb);
+    cur.h = small ? (static_cast<int>(wlo) - HKV * pb) / cur.nb
+                  : static_cast<int>((wlo - static_cast<long long>(HKV) * pb) / cur.nb);
     cur.S = static_cast<long long>(HKV) * pb + static_cast<long long>(cur.h) * cur.nb;
-    cur.x = lo;
-    const long long e = cur.S + cur.nb < hi ? cur.S + cur.nb : hi;
-    cur.nblk = static_cast<int>(e - lo < 64 ? e - lo : 64);
+    cur.x = wlo;
+    const long long e = cur.S + cur.nb < whi ? cur.S + cur.nb : whi;
+    cur.nblk = static_cast<int>(e - wlo < 64 ? e - wlo : 64);
   }
-  float* part_o = reinterpret_cast<float*>(a.ws + FL.o);
-  float* part_ml = reinterpret_cast<float*>(a.ws + FL.ml);
-
   constexpr int kElem = (KV == DT_BF16) ? 2 : 1;
   const size_t head_bytes = static_cast<size_t>(kBS) * kD * kElem;
   Raw<KV> kbuf[2], vbuf[2];
@@ -392,8 +430,8 @@ __global__ __launch_bounds__(64, 2) void decode_mfma_flat_kernel(DecodeArgs a) {
   const_i32p lens = (const_i32p)(a.context_lens);
   const_i32p table = (const_i32p)(a.block_table);
   auto seg_bounds = [&](const Cursor& c, int& jb, int& je) {
-    const long long s0 = c.S > lo ? c.S : lo;
-    const long long s1 = c.S + c.nb < hi ? c.S + c.nb : hi;
+    const long long s0 = c.S > wlo ? c.S : wlo;
+    const long long s1 = c.S + c.nb < whi ? c.S + c.nb : whi;
     jb = static_cast<int>(s0 - c.S) + skip;
     je = static_cast<int>(s1 - c.S) + skip;
   };
@@ -411,9 +449,7 @@ __global__ __launch_bounds__(64, 2) void decode_mfma_flat_kernel(DecodeArgs a) {
   }
   issue(kbuf[0], vbuf[0], __builtin_amdgcn_readlane(win0, 0), cur.h);
   issue(kbuf[1], vbuf[1], __builtin_amdgcn_readlane(win0, min(1, cur.nblk - 1)), cur.h);
-  Acc<NG> acc;
   acc_init<NG>(acc);
-  int slot = 0;
 
   // One group: blocks [c.x, c.x + c.nblk) of sequence (c.b, c.h) with n
   // cached positions and table entries `win`; the loads of its first two
@@ -426,7 +462,7 @@ __global__ __launch_bounds__(64, 2) void decode_mfma_flat_kernel(DecodeArgs a) {
   // window still on its way is never copied (a copy would wait for every
   // load in flight).
   auto group = [&](const Cursor& c, int n, int win, Cursor& nxt, int& win_nxt, int& n_nxt) {
-    nxt = next_group(c, hi, prefix, B, HKV);
+    nxt = next_group(c, whi, prefix, B, HKV);
     const bool more = nxt.nblk > 0;
     const bool new_seq = more && nxt.x == nxt.S;
     win_nxt = load_window(a, nxt, skip, L.lane);
@@ -494,10 +530,31 @@ __global__ __launch_bounds__(64, 2) void decode_mfma_flat_kernel(DecodeArgs a) {
       i0 += 2;
     } while (i0 < nsteps);
     if (!more || new_seq) {
-      // the sequence's part in this chunk is done
+      // the sequence's part in this wave's range is done; what is written
+      // follows the workgroup's chunk [lo, hi)
       const long long S = c.S, E = c.S + c.nb;
       const size_t hq0 = static_cast<size_t>(c.b) * a.H_Q + static_cast<size_t>(c.h) * a.g;
-      if (S >= lo && E <= hi && a.cascade) {
+      if (HW > 1 && hw > 0 && S < wlo) {
+        // cut at this wave's start: its piece goes to the wave's LDS slot
+#pragma unroll
+        for (int G = 0; G < NG; ++G) {
+          float* pg = piece_lds + (hw - 1) * kSlot + G * 34 * 64 + L.lane;
+#pragma unroll
+          for (int nn = 0; nn < 8; ++nn)
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii) pg[(4 * nn + ii) * 64] = acc.o[G][nn][ii];
+          pg[32 * 64] = acc.m[G];
+          pg[33 * 64] = acc.l[G];
+        }
+      } else if (HW > 1 && E > whi && whi < hi) {
+        // it continues into the next wave's part: keep it for the merge (the
+        // walk ends here)
+        held = true;
+        held_b = c.b;
+        held_h = c.h;
+        held_S = S;
+        held_E = E;
+      } else if (S >= lo && E <= hi && a.cascade) {
         // whole sequence of a cascade: a piece, merged with the prefix pieces
         const CascadeLayout CL = cascade_layout(B, a.H_Q, W, a.g, kD, a.prefix_splits);
         write_state<NG>(acc, L, a.g, nullptr,
@@ -506,10 +563,11 @@ __global__ __launch_bounds__(64, 2) void decode_mfma_flat_kernel(DecodeArgs a) {
       } else if (S >= lo && E <= hi) {
         write_state<NG>(acc, L, a.g, a.out + hq0 * kD, nullptr, 0, nullptr, 0);
       } else {
+        // slot 0: the chunk's first sequence (it holds block lo); slot 1: its last
+        const int slot = S <= lo ? 0 : 1;
         const size_t base = (static_cast<size_t>(w) * 2 + slot) * a.g;
         write_state<NG>(acc, L, a.g, nullptr, part_o + base * kD, kD, part_ml + base * 2, 2);
       }
-      slot = 1;
       if (new_seq) {
         acc_init<NG>(acc);
         if constexpr (FUSED) {
@@ -526,12 +584,54 @@ __global__ __launch_bounds__(64, 2) void decode_mfma_flat_kernel(DecodeArgs a) {
   int win1, n1;
   while (group(cur, n0, win0, cur1, win1, n1) && group(cur1, n1, win1, cur, win0, n0)) {
   }
+  }  // wlo < whi
+
+  if constexpr (HW > 1) {
+    __syncthreads();  // the later waves' pieces are in LDS
+    if (held) {
+      // merge the pieces of the following waves that cover the sequence: all
+      // use the same lane layout, and a lane's (m, l) belong to its own
+      // column and dims
+      for (int j = hw + 1; j < HW; ++j) {
+        const long long qj = lo + min(j * part, hi - lo);
+        const long long qj1 = lo + min((j + 1) * part, hi - lo);
+        if (qj >= qj1 || held_E <= qj) break;  // wave j has nothing of it
+#pragma unroll
+        for (int G = 0; G < NG; ++G) {
+          const float* pg = piece_lds + (j - 1) * kSlot + G * 34 * 64 + L.lane;
+          const float m1 = pg[32 * 64], l1 = pg[33 * 64];
+          const float mn = fmaxf(acc.m[G], m1);
+          const float f0 = acc.m[G] == mn ? 1.0f : __builtin_amdgcn_exp2f(acc.m[G] - mn);
+          const float f1 = m1 == mn ? 1.0f : __builtin_amdgcn_exp2f(m1 - mn);
+          acc.l[G] = acc.l[G] * f0 + l1 * f1;
+#pragma unroll
+          for (int nn = 0; nn < 8; ++nn)
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii)
+              acc.o[G][nn][ii] = acc.o[G][nn][ii] * f0 + pg[(4 * nn + ii) * 64] * f1;
+          acc.m[G] = mn;
+        }
+      }
+      const size_t hq0 = static_cast<size_t>(held_b) * a.H_Q + static_cast<size_t>(held_h) * a.g;
+      if (held_S >= lo && held_E <= hi) {
+        write_state<NG>(acc, L, a.g, a.out + hq0 * kD, nullptr, 0, nullptr, 0);
+      } else {
+        const int slot = held_S <= lo ? 0 : 1;
+        const size_t base = (static_cast<size_t>(w) * 2 + slot) * a.g;
+        write_state<NG>(acc, L, a.g, nullptr, part_o + base * kD, kD, part_ml + base * 2, 2);
+      }
+    }
+  }
 }
 
 // The fused append keeps the new row in registers for the whole walk: with
 // bf16 caches and one head group that fits (the bf16 kernel runs one wave
-// per SIMD anyway); fp8 would lose a wave per SIMD and two head groups
-// would spill, so those cases launch the append kernel first.
+// per SIMD anyway).  For fp8 caches the row is quantised with its block's
+// scale, which the walk has only when it reaches the block: done there, the
+// division, encoding and store at every sequence's last block cost the fp8
+// walk more than the append launch they save (measured on MI355X: fp8 GQA
+// step 175 vs 174 us, fp8 MHA 643 vs 588 us), so fp8 and two head groups
+// launch the append kernel first.
 bool mfma_fuses_append(int kv_dtype, int g) { return kv_dtype == DT_BF16 && g <= 16; }
 
 bool mfma_supports(int q_dtype, int kv_dtype, int d_h, int block_size, int g) {
@@ -544,24 +644,59 @@ namespace {
 // blocks are processed in pairs, so the distance must be odd).
 constexpr int kDepth = 1;
 
-template <int KV, int NG, bool FUSED = false>
-const void* mfma_kernel_ptr(bool flat, bool cascade) {
-  if (!flat) return reinterpret_cast<const void*>(&decode_mfma_kernel<KV, NG, kDepth, FUSED>);
-  return cascade
-             ? reinterpret_cast<const void*>(&decode_mfma_flat_kernel<KV, NG, FUSED, true>)
-             : reinterpret_cast<const void*>(&decode_mfma_flat_kernel<KV, NG, FUSED, false>);
+struct KernelPick {
+  const void* fn;
+  int waves_per_group;  // waves of one workgroup (64 lanes each)
+};
+
+// Waves per chunk of the flat grid (no cascade).  fp8 tiles carry half the
+// bytes for the same per-block chain of dependent products, so with several
+// query heads per KV head the walks are latency bound and more walks per
+// SIMD pay, best as four waves on each of half as many chunks (fewer cut
+// sequences); with one query head per KV head there is little work per
+// block and one wave per chunk at full occupancy streams best; bf16 walks
+// stream best one per SIMD.  Measured on MI355X, kernel us with 1 / 2 / 4
+// waves per chunk: fp8 MQA 40.6 / 37.0 / 34.4, fp8 GQA 159.8 / 152.9 /
+// 152.6, fp8 MHA 568.6 (full occupancy) / - / 582.2, 8B-style bf16 batch
+// 54.5 / 55.6 / 55.4, 32K bf16 161.5 / 164.0 / 162.5.  PKV_FLAT_SPLIT (1, 2
+// or 4) overrides it, for tuning measurements.
+int flat_split(int kv_dtype, int g) {
+  static const int forced = [] {
+    const char* e = std::getenv("PKV_FLAT_SPLIT");
+    const int v = e ? std::atoi(e) : 0;
+    return (v == 1 || v == 2 || v == 4) ? v : 0;
+  }();
+  if (forced) return forced;
+  return kv_dtype == DT_FP8 && g >= 4 ? 4 : 1;
 }
 
-// fused: the append runs inside the launch (bf16 caches, one head group;
-// see mfma_fuses_append); cascade: the flat grid also does the prefix work
-const void* pick_kernel(int kv_dtype, int g, bool flat, bool fused, bool cascade) {
-  const bool two = g > 16;
-  if (kv_dtype == DT_BF16) {
-    if (fused && !two) return mfma_kernel_ptr<DT_BF16, 1, true>(flat, cascade);
-    return two ? mfma_kernel_ptr<DT_BF16, 2>(flat, cascade)
-               : mfma_kernel_ptr<DT_BF16, 1>(flat, cascade);
+template <int KV, int NG, bool FUSED = false>
+KernelPick mfma_kernel_ptr(bool flat, bool cascade, int split) {
+  if (!flat) return {reinterpret_cast<const void*>(&decode_mfma_kernel<KV, NG, kDepth, FUSED>), 1};
+  if (cascade)
+    return {reinterpret_cast<const void*>(&decode_mfma_flat_kernel<KV, NG, FUSED, true>), 1};
+  switch (split) {
+    case 2:
+      return {reinterpret_cast<const void*>(&decode_mfma_flat_kernel<KV, NG, FUSED, false, 2>), 2};
+    case 4:
+      return {reinterpret_cast<const void*>(&decode_mfma_flat_kernel<KV, NG, FUSED, false, 4>), 4};
+    default:
+      return {reinterpret_cast<const void*>(&decode_mfma_flat_kernel<KV, NG, FUSED, false, 1>), 1};
   }
-  return two ? mfma_kernel_ptr<DT_FP8, 2>(flat, cascade) : mfma_kernel_ptr<DT_FP8, 1>(flat, cascade);
+}
+
+// fused: the append runs inside the launch (see mfma_fuses_append);
+// cascade: the flat grid also does the prefix work
+KernelPick pick_kernel(int kv_dtype, int g, bool flat, bool fused, bool cascade) {
+  const bool two = g > 16;
+  const int split = flat_split(kv_dtype, g);
+  if (kv_dtype == DT_BF16) {
+    if (fused && !two) return mfma_kernel_ptr<DT_BF16, 1, true>(flat, cascade, split);
+    return two ? mfma_kernel_ptr<DT_BF16, 2>(flat, cascade, split)
+               : mfma_kernel_ptr<DT_BF16, 1>(flat, cascade, split);
+  }
+  return two ? mfma_kernel_ptr<DT_FP8, 2>(flat, cascade, split)
+             : mfma_kernel_ptr<DT_FP8, 1>(flat, cascade, split);
 }
 }  // namespace
 
@@ -577,32 +712,45 @@ const void* pick_kernel(int kv_dtype, int g, bool flat, bool fused, bool cascade
 // full occupancy; fp8 MQA, W = 512 / 1024 / 1536 / 2048 / 3072: 53.1 / 40.6 /
 // 41.1 / 44.0 / 54.6 us.)
 int mfma_flat_waves(int kv_dtype, int g, int B, bool cascade) {
-  const void* k = pick_kernel(kv_dtype, g, true, cascade && mfma_fuses_append(kv_dtype, g),
-                              cascade);
+  // the occupancy of the variant with the fused append where one exists
+  // (the step launches it; it needs at least the registers of the other)
+  const KernelPick k = pick_kernel(kv_dtype, g, true, mfma_fuses_append(kv_dtype, g), cascade);
   int dev = 0, cus = 0, per_cu = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k, 64,
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k.fn, 64 * k.waves_per_group,
                                                    sizeof(int32_t) * (B + 1)) != hipSuccess ||
       cus <= 0 || per_cu <= 0) {
     (void)hipGetLastError();
     return 256 * 4;
   }
+  // per_cu counts workgroups (chunks) of waves_per_group waves.  Waves per
+  // SIMD: one for bf16, and for two head groups with one wave per chunk;
+  // two for fp8 split chunks; what the occupancy allows for fp8 with one
+  // head group and one wave per chunk.
   const int simds_per_cu = 4;
-  if (kv_dtype == DT_BF16 || g > 16) per_cu = per_cu < simds_per_cu ? per_cu : simds_per_cu;
-  return cus * per_cu;
+  int per_simd = 0;  // 0: the occupancy
+  if (kv_dtype == DT_BF16 || (g > 16 && k.waves_per_group == 1)) per_simd = 1;
+  else if (k.waves_per_group > 1) per_simd = 2;
+  if (per_simd > 0) {
+    const int cap = simds_per_cu * per_simd / k.waves_per_group;
+    per_cu = per_cu < cap ? per_cu : cap;
+  }
+  return cus * (per_cu > 0 ? per_cu : 1);
 }
 
 hipError_t launch_decode_mfma(int kv_dtype, bool flat, int waves, const DecodeArgs& a,
                               hipStream_t stream) {
   const bool cascade = a.cascade != 0;
-  const void* k = pick_kernel(kv_dtype, a.g, flat, a.k_new != nullptr, cascade);
+  const KernelPick k = pick_kernel(kv_dtype, a.g, flat, a.k_new != nullptr, cascade);
   void* args[] = {const_cast<DecodeArgs*>(&a)};
   if (flat) {
+    // `waves` chunks, one workgroup each
     const int grid = waves + (cascade ? a.prefix_waves : 0);
-    return hipLaunchKernel(k, dim3(grid), dim3(64), args, sizeof(int32_t) * (a.B + 1), stream);
+    return hipLaunchKernel(k.fn, dim3(grid), dim3(64 * k.waves_per_group), args,
+                           sizeof(int32_t) * (a.B + 1), stream);
   }
-  return hipLaunchKernel(k, dim3(a.max_parts, a.H_KV, a.B), dim3(64), args, 0, stream);
+  return hipLaunchKernel(k.fn, dim3(a.max_parts, a.H_KV, a.B), dim3(64), args, 0, stream);
 }
 
 }  // namespace pkv

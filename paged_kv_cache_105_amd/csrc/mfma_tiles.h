@@ -165,7 +165,7 @@ struct LaneMap {
 
 __device__ __forceinline__ LaneMap lane_map() {
   LaneMap L;
-  L.lane = threadIdx.x;
+  L.lane = threadIdx.x & 63;  // lane within the wave (a workgroup may hold several)
   L.q4 = L.lane >> 4;
   L.c = L.lane & 15;
 #pragma unroll

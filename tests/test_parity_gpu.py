@@ -214,6 +214,29 @@ def test_fp8_append_exhaustive_bf16_inputs():
     assert np.array_equal(as_numpy(vc), rv)
 
 
+@pytest.mark.parametrize("H_Q", [1, 32], ids=["g1", "g32"])
+def test_fp8_fused_append_exhaustive_bf16_inputs(H_Q):
+    # pkv_decode_step on an fp8 cache (its append, then the flat walk with
+    # one or two head groups per wave): every bf16 bit pattern x 4 scales;
+    # the pools must equal the oracle's append byte for byte
+    B, H_KV, d_h = 512, 1, 128
+    pats = torch.arange(65536, dtype=torch.int32).to(torch.int16).view(torch.bfloat16)
+    w = make_workload("fp8_mha", lens_after=[1] * B, H_KV=H_KV, H_Q=H_Q, pool_factor=1.0)
+    assert w.num_blocks == B
+    scales = torch.tensor([1.0, 2.0 ** -3, 0.37, 3.1], dtype=torch.float32)
+    w.k_new[0] = pats.reshape(B, H_KV, d_h).clone()
+    w.v_new[0] = pats.flip(0).reshape(B, H_KV, d_h).clone()
+    w.k_scale[0] = scales[torch.arange(B) % 4].reshape(B, 1).clone()
+    w.v_scale[0] = scales[(torch.arange(B) + 1) % 4].reshape(B, 1).clone()
+    kc, vc, _ = _fused_step(w, pkv.PKV_VARIANT_MFMA)
+    d = _np(w)
+    rk, rv = paged.append(d["k_cache"], d["v_cache"], w.kv_dtype, d["k_new"], d["v_new"],
+                          w.q_dtype, d["table"], d["lens"], w.block_size, d["k_scale"],
+                          d["v_scale"])
+    assert np.array_equal(as_numpy(kc), rk)
+    assert np.array_equal(as_numpy(vc), rv)
+
+
 @pytest.mark.parametrize("variant", VARIANTS, ids=VIDS)
 def test_fp8_every_finite_code_decodes_exactly(variant):
     # n = 1: the output is the appended value itself; with scale 1 the
