@@ -532,9 +532,14 @@ def decode_measure(args, name, dev, full=True):
         for i in range(args.steps):
             for L in range(w.layers):
                 kc, vc = pools[i % R][L]
-                pkv.decode_partitions(out, w.q[L], kc, vc, w.block_table, w.context_lens,
-                                      w.max_context_len, w.softmax_scale, ks[L], vs[L],
-                                      partition_tokens=pt, workspace=work, stream=stream)
+                if cascade:
+                    pkv.cascade_partitions(out, w.q[L], kc, vc, w.block_table, w.context_lens,
+                                           w.max_context_len, w.softmax_scale, w.shared_blocks,
+                                           ks[L], vs[L], workspace=work, stream=stream)
+                else:
+                    pkv.decode_partitions(out, w.q[L], kc, vc, w.block_table, w.context_lens,
+                                          w.max_context_len, w.softmax_scale, ks[L], vs[L],
+                                          partition_tokens=pt, workspace=work, stream=stream)
         e1.record(stream)
         torch.cuda.synchronize()
         kern_ms.append(e0.elapsed_time(e1) / (args.steps * w.layers))
@@ -543,6 +548,11 @@ def decode_measure(args, name, dev, full=True):
 
     att = metrics.attention_bytes(lens, w.H_Q, w.H_KV, w.d_h, w.block_size, w.kv_dtype,
                                   w.q_dtype)
+    logical_bytes = att["total"]
+    if cascade:
+        # the shared prefix is read once per layer for the whole batch
+        att = metrics.cascade_attention_bytes(lens, w.shared_blocks, w.H_Q, w.H_KV, w.d_h,
+                                              w.block_size, w.kv_dtype, w.q_dtype)
     app = metrics.append_bytes(w.B, w.H_KV, w.d_h, w.kv_dtype, w.q_dtype)
     step_bytes = w.layers * (att["total"] + app)
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
@@ -556,12 +566,17 @@ def decode_measure(args, name, dev, full=True):
         f"{100 * achieved / PEAK_GBS:.1f}% of peak")
     kernel = {0: "decode_mfma_flat_kernel", 1: "decode_generic_kernel",
               2: "decode_mfma_flat_kernel", 3: "decode_mfma_kernel"}[args.variant]
+    if cascade:
+        kernel = "decode_mfma_flat_kernel (cascade: prefix and private waves)"
     rec = {"value": round(value, 2), "ms_per_step": round(ms_per_step, 5),
            "config": {"workload": name, "B": w.B, "H_Q": w.H_Q, "H_KV": w.H_KV,
                       "d_h": w.d_h, "block_size": w.block_size, "kv_dtype": w.kv_dtype,
                       "q_dtype": w.q_dtype, "layers": w.layers, "partition_tokens": pt,
                       "partitions_max": parts, "pool_copies": R,
                       "cascade_shared_blocks": w.shared_blocks if cascade else 0,
+                      "bytes_counted": "unique (shared prefix once per layer)" if cascade
+                      else "every request's positions",
+                      "logical_bytes_per_layer": logical_bytes,
                       "mean_context": round(sum(lens) / len(lens), 1),
                       "us_per_step_per_layer": round(ms_per_step * 1e3 / w.layers, 2),
                       "pct_of_peak_step": round(100 * value / PEAK_GBS, 2)},

@@ -382,6 +382,21 @@ int pkv_decode_step_cascade(const void* k_new, const void* v_new, float* out, co
                             int32_t num_blocks, float softmax_scale, int32_t shared_blocks,
                             void* workspace, size_t workspace_bytes, pkv_stream_t stream);
 
+/* The attention launch of pkv_decode_step_cascade alone (no append, no
+ * combine), for timing that kernel: the same arguments without k_new /
+ * v_new; it leaves the prefix pieces and the private pieces in the
+ * workspace and writes nothing to `out` that the combine would not
+ * overwrite.  The results are complete only after the combine, which only
+ * pkv_decode_step_cascade launches. */
+int pkv_cascade_partitions(float* out, const void* q, int q_dtype, const void* k_cache,
+                           const void* v_cache, int kv_dtype, const float* k_scale,
+                           const float* v_scale, const int32_t* block_table,
+                           int32_t max_blocks_per_seq, const int32_t* context_lens,
+                           int32_t max_context_len, int32_t B, int32_t H_Q, int32_t H_KV,
+                           int32_t d_h, int32_t block_size, int32_t num_blocks,
+                           float softmax_scale, int32_t shared_blocks, void* workspace,
+                           size_t workspace_bytes, pkv_stream_t stream);
+
 /* The two launches of pkv_paged_decode_attention, callable separately (for
  * timing each kernel).  decode_partitions runs the online softmax over each
  * piece (same arguments); it writes `out` directly for requests whose

@@ -15,7 +15,7 @@ from . import _lib
 from ._lib import (PKV_BF16, PKV_F32, PKV_FP8_E4M3, PKV_VARIANT_AUTO, PKV_VARIANT_GENERIC,
                    PKV_VARIANT_MFMA, PKV_VARIANT_MFMA_PARTITION, PkvError, check, load)
 
-__all__ = ["kv_append", "copy_blocks", "decode_plan", "decode_workspace_size", "decode_step_noalloc", "paged_decode_attention", "decode_partitions",
+__all__ = ["kv_append", "copy_blocks", "decode_plan", "decode_workspace_size", "decode_step_noalloc", "cascade_partitions", "paged_decode_attention", "decode_partitions",
            "combine_partitions", "set_decode_variant", "BlockPool", "PkvError", "load",
            "prefix_root", "block_hashes", "DIGEST_BYTES", "kv_append_chunk",
            "paged_chunk_attention", "swap_record_bytes", "swap_out", "swap_in", "decode_step",
@@ -254,6 +254,21 @@ def decode_step_cascade(k_new, v_new, out, q, k_cache, v_cache, block_table, con
         block_table.shape[1], _ptr(context_lens), int(max_context_len), B, H_Q, H_KV, d_h, bs,
         num_blocks, softmax_scale, int(shared_blocks), _ptr(workspace), ws_bytes,
         _stream(stream)), "pkv_decode_step_cascade")
+
+
+def cascade_partitions(out, q, k_cache, v_cache, block_table, context_lens, max_context_len,
+                       softmax_scale, shared_blocks, k_scale=None, v_scale=None, workspace=None,
+                       stream=None):
+    """pkv_cascade_partitions: the cascade's attention kernel alone."""
+    B, H_Q, d_h = q.shape
+    num_blocks, H_KV, bs, _ = k_cache.shape
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    check(load().pkv_cascade_partitions(
+        _ptr(out), _ptr(q), _dtype_code(q), _ptr(k_cache), _ptr(v_cache), _dtype_code(k_cache),
+        _ptr(k_scale), _ptr(v_scale), _ptr(block_table), block_table.shape[1],
+        _ptr(context_lens), int(max_context_len), B, H_Q, H_KV, d_h, bs, num_blocks,
+        softmax_scale, int(shared_blocks), _ptr(workspace), ws_bytes, _stream(stream)),
+        "pkv_cascade_partitions")
 
 
 def decode_partitions(out, q, k_cache, v_cache, block_table, context_lens, max_context_len,

@@ -74,6 +74,9 @@ SIGNATURES = {
     "pkv_decode_step_cascade": (C.c_int, [_vp, _vp, _vp, _vp, C.c_int, _vp, _vp, C.c_int, _vp,
                                           _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32,
                                           _i32, _i32, _f, _i32, _vp, _sz, _vp]),
+    "pkv_cascade_partitions": (C.c_int, [_vp, _vp, C.c_int, _vp, _vp, C.c_int, _vp, _vp, _vp,
+                                         _i32, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f,
+                                         _i32, _vp, _sz, _vp]),
     "pkv_decode_partitions": (C.c_int, [_vp, _vp, C.c_int, _vp, _vp, C.c_int, _vp, _vp, _vp,
                                         _i32, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f,
                                         _i32, _vp, _sz, _vp]),

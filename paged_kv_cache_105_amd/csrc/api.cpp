@@ -708,14 +708,19 @@ int pkv_cascade_plan(int32_t B, int32_t H_Q, int32_t H_KV, int32_t d_h, int32_t 
   return PKV_OK;
 }
 
-int pkv_decode_step_cascade(const void* k_new, const void* v_new, float* out, const void* q,
-                            int q_dtype, void* k_cache, void* v_cache, int kv_dtype,
-                            const float* k_scale, const float* v_scale,
-                            const int32_t* block_table, int32_t max_blocks_per_seq,
-                            const int32_t* context_lens, int32_t max_context_len, int32_t B,
-                            int32_t H_Q, int32_t H_KV, int32_t d_h, int32_t block_size,
-                            int32_t num_blocks, float softmax_scale, int32_t shared_blocks,
-                            void* workspace, size_t workspace_bytes, pkv_stream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// The cascade step; with_combine = false launches the attention kernel only
+// (no append may be asked for then).
+int cascade_step(const void* k_new, const void* v_new, float* out, const void* q, int q_dtype,
+                 void* k_cache, void* v_cache, int kv_dtype, const float* k_scale,
+                 const float* v_scale, const int32_t* block_table, int32_t max_blocks_per_seq,
+                 const int32_t* context_lens, int32_t max_context_len, int32_t B, int32_t H_Q,
+                 int32_t H_KV, int32_t d_h, int32_t block_size, int32_t num_blocks,
+                 float softmax_scale, int32_t shared_blocks, void* workspace,
+                 size_t workspace_bytes, pkv_stream_t stream, bool with_combine) {
   int st = check_attention_args(out, q, q_dtype, k_cache, v_cache, kv_dtype, k_scale, v_scale,
                                 block_table, max_blocks_per_seq, context_lens, max_context_len,
                                 B, H_Q, H_KV, d_h, block_size, num_blocks, softmax_scale);
@@ -776,10 +781,43 @@ int pkv_decode_step_cascade(const void* k_new, const void* v_new, float* out, co
     a.v_new = v_new;
   }
   hipError_t e = pkv::launch_decode_mfma(kv_dtype, true, plan.waves, a, s);
-  if (e != hipSuccess) return hip_status(e);
+  if (e != hipSuccess || !with_combine) return hip_status(e);
   return hip_status(pkv::launch_combine(out, context_lens, workspace, workspace_bytes, B, H_Q,
                                         H_KV, d_h, plan.partition_tokens, plan.max_parts, splits,
                                         s));
+}
+
+}  // namespace
+
+extern "C" {
+
+int pkv_decode_step_cascade(const void* k_new, const void* v_new, float* out, const void* q,
+                            int q_dtype, void* k_cache, void* v_cache, int kv_dtype,
+                            const float* k_scale, const float* v_scale,
+                            const int32_t* block_table, int32_t max_blocks_per_seq,
+                            const int32_t* context_lens, int32_t max_context_len, int32_t B,
+                            int32_t H_Q, int32_t H_KV, int32_t d_h, int32_t block_size,
+                            int32_t num_blocks, float softmax_scale, int32_t shared_blocks,
+                            void* workspace, size_t workspace_bytes, pkv_stream_t stream) {
+  return cascade_step(k_new, v_new, out, q, q_dtype, k_cache, v_cache, kv_dtype, k_scale, v_scale,
+                      block_table, max_blocks_per_seq, context_lens, max_context_len, B, H_Q,
+                      H_KV, d_h, block_size, num_blocks, softmax_scale, shared_blocks, workspace,
+                      workspace_bytes, stream, true);
+}
+
+int pkv_cascade_partitions(float* out, const void* q, int q_dtype, const void* k_cache,
+                           const void* v_cache, int kv_dtype, const float* k_scale,
+                           const float* v_scale, const int32_t* block_table,
+                           int32_t max_blocks_per_seq, const int32_t* context_lens,
+                           int32_t max_context_len, int32_t B, int32_t H_Q, int32_t H_KV,
+                           int32_t d_h, int32_t block_size, int32_t num_blocks,
+                           float softmax_scale, int32_t shared_blocks, void* workspace,
+                           size_t workspace_bytes, pkv_stream_t stream) {
+  return cascade_step(nullptr, nullptr, out, q, q_dtype, const_cast<void*>(k_cache),
+                      const_cast<void*>(v_cache), kv_dtype, k_scale, v_scale, block_table,
+                      max_blocks_per_seq, context_lens, max_context_len, B, H_Q, H_KV, d_h,
+                      block_size, num_blocks, softmax_scale, shared_blocks, workspace,
+                      workspace_bytes, stream, false);
 }
 
 }  // extern "C"

@@ -409,7 +409,13 @@ __global__ __launch_bounds__(64 * HW, 2) void decode_mfma_flat_kernel(DecodeArgs
   constexpr int kElem = (KV == DT_BF16) ? 2 : 1;
   const size_t head_bytes = static_cast<size_t>(kBS) * kD * kElem;
   Raw<KV> kbuf[2], vbuf[2];
-  // load block id p (clamped into the pool) of KV head hh
+  // load block id p (clamped into the pool) of KV head hh.  Steps that only
+  // keep the load count even -- the padding step of a group with an odd
+  // number of blocks, and the loads past the end of the walk -- load the
+  // tile of block 0, KV head 0 instead of re-reading a block: the stream's
+  // loads bypass the caches, so a re-read goes back to HBM, while the one
+  // tile every wave uses that way stays cached (the data is never used: a
+  // padding step masks every position).
   auto issue = [&](Raw<KV>& kr, Raw<KV>& vr, int p, int hh) {
     p = min(max(p, 0), a.num_blocks - 1);
     const size_t off = (static_cast<size_t>(p) * HKV + hh) * head_bytes;
@@ -448,7 +454,8 @@ __global__ __launch_bounds__(64 * HW, 2) void decode_mfma_flat_kernel(DecodeArgs
     new_row_load(a, L, cur.b, cur.h, nr);
   }
   issue(kbuf[0], vbuf[0], __builtin_amdgcn_readlane(win0, 0), cur.h);
-  issue(kbuf[1], vbuf[1], __builtin_amdgcn_readlane(win0, min(1, cur.nblk - 1)), cur.h);
+  issue(kbuf[1], vbuf[1], cur.nblk > 1 ? __builtin_amdgcn_readlane(win0, 1) : 0,
+        cur.nblk > 1 ? cur.h : 0);
   acc_init<NG>(acc);
 
   // One group: blocks [c.x, c.x + c.nblk) of sequence (c.b, c.h) with n
@@ -470,7 +477,7 @@ __global__ __launch_bounds__(64 * HW, 2) void decode_mfma_flat_kernel(DecodeArgs
     if (more) {
       const size_t e = static_cast<size_t>(nxt.b) * cap + static_cast<int>(nxt.x - nxt.S) + skip;
       p_nxt0 = table[e];
-      p_nxt1 = nxt.nblk > 1 ? table[e + 1] : p_nxt0;
+      p_nxt1 = nxt.nblk > 1 ? table[e + 1] : 0;  // 0: the padding tile
     }
     const int n_raw_nxt = new_seq ? lens[nxt.b] : n;
     n_nxt = min(n_raw_nxt, cap * kBS);
@@ -517,13 +524,15 @@ __global__ __launch_bounds__(64 * HW, 2) void decode_mfma_flat_kernel(DecodeArgs
         // the load of step i + 2, into the buffer this step has used
         const int j = i + 2;
         int p, hh = c.h;
-        if (j < nsteps) {
-          p = __builtin_amdgcn_readlane(win, min(j, c.nblk - 1));
+        if (j < c.nblk) {
+          p = __builtin_amdgcn_readlane(win, j);
+        } else if (j < nsteps) {
+          p = hh = 0;  // the padding step
         } else if (more) {
           p = j == nsteps ? p_nxt0 : p_nxt1;
-          hh = nxt.h;
+          hh = j == nsteps || nxt.nblk > 1 ? nxt.h : 0;
         } else {
-          p = __builtin_amdgcn_readlane(win, c.nblk - 1);
+          p = hh = 0;  // past the end of the walk
         }
         issue(kbuf[u], vbuf[u], p, hh);
       }

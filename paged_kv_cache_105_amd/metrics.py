@@ -35,6 +35,33 @@ def attention_bytes(lens, H_Q, H_KV, d_h, block_size, kv_dtype, q_dtype) -> dict
                 total=kv + scales + q + out + table)
 
 
+def cascade_attention_bytes(lens, shared_blocks, H_Q, H_KV, d_h, block_size, kv_dtype,
+                            q_dtype) -> dict:
+    """The step's bytes when every request's table starts with the same
+    ``shared_blocks`` blocks and every context covers them: the shared
+    positions are read once for the batch (page 2 "KV Cache Explained",
+    section "Prefix reuse saves prefill, while decode still needs the
+    history": one physical copy serves every request), each request's
+    other positions once for itself.  Same other terms as
+    ``attention_bytes`` (the shared table entries read once)."""
+    s = DTYPE_BYTES[kv_dtype]
+    sq = DTYPE_BYTES[q_dtype]
+    lens = [int(n) for n in lens]
+    shared = shared_blocks * block_size
+    if any(n <= shared for n in lens):
+        raise ValueError("every context must cover the shared blocks")
+    positions = shared + sum(n - shared for n in lens)
+    kv = 2 * H_KV * positions * d_h * s
+    blocks = shared_blocks + sum(_ceil_div(n, block_size) - shared_blocks for n in lens)
+    scales = 2 * H_KV * blocks * 4 if kv_dtype == "fp8_e4m3" else 0
+    B = len(lens)
+    q = B * H_Q * d_h * sq
+    out = B * H_Q * d_h * 4
+    table = blocks * 4 + B * 4
+    return dict(kv=kv, scales=scales, q=q, out=out, table=table,
+                total=kv + scales + q + out + table)
+
+
 def append_bytes(B, H_KV, d_h, kv_dtype, in_dtype, block_size=None) -> int:
     s = DTYPE_BYTES[kv_dtype]
     si = DTYPE_BYTES[in_dtype]

@@ -99,3 +99,27 @@ def test_append_bytes_by_hand():
     # and the table entry and length of every request
     assert metrics.append_bytes(3, 2, 8, "fp8_e4m3", "bf16") == \
         2 * 3 * 2 * 8 * (2 + 1) + 2 * 3 * 2 * 4 + 8 * 3
+
+
+def test_cascade_bytes_count_each_distinct_slot_once():
+    # brute force over the shared-prefix batch: the distinct (physical
+    # block, slot) pairs the requests read, each worth one position of K and
+    # V for every KV head (page 3 "xf_kv_cache", "End-to-end flow": the
+    # prefix's 75 blocks are mapped by every request)
+    w = make_workload("shared_prefix", layers=1, values=False)
+    table, lens = w.block_table.tolist(), [int(n) for n in w.context_lens]
+    read = set()
+    for row, n in zip(table, lens):
+        for t in range(n):
+            read.add((row[t // w.block_size], t % w.block_size))
+    att = metrics.cascade_attention_bytes(lens, w.shared_blocks, w.H_Q, w.H_KV, w.d_h,
+                                          w.block_size, w.kv_dtype, w.q_dtype)
+    assert att["kv"] == len(read) * PER_POS[("bf16", 8)]
+    assert w.shared_blocks == 75
+    # and the physical blocks behind them, as the oracle counts them
+    blocks = kvbytes.unique_block_bytes(table, lens, w.block_size, 1)
+    assert att["table"] == 4 * blocks + 4 * w.B
+    # the logical count reads the shared positions once per request
+    logical = metrics.attention_bytes(lens, w.H_Q, w.H_KV, w.d_h, w.block_size, w.kv_dtype,
+                                      w.q_dtype)
+    assert logical["kv"] - att["kv"] == (w.B - 1) * 75 * 16 * PER_POS[("bf16", 8)]

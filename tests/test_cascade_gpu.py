@@ -122,3 +122,28 @@ def test_cascade_rejects_bad_shapes():
     with pytest.raises(pkv.PkvError) as e:
         pkv.cascade_plan(4, 32, 8, 128, 16, 100, 7)   # prefix longer than the contexts
     assert e.value.name == "invalid_arg"
+
+
+def test_cascade_partitions_launches_the_attention_kernel_alone():
+    # pkv_cascade_partitions (for timing the cascade's attention kernel):
+    # no append (the pools are untouched) and a step run after it on the same
+    # workspace still matches the oracle
+    w = make_workload("shared_prefix", layers=1, B=6)
+    g = lambda t: t.to(DEV).contiguous()
+    kc, vc = g(w.k_cache[0]), g(w.v_cache[0])
+    k0, v0 = kc.clone(), vc.clone()
+    bt, cl = g(w.block_table), g(w.context_lens)
+    _, ws = pkv.cascade_plan(w.B, w.H_Q, w.H_KV, w.d_h, w.block_size, w.max_context_len, 75)
+    work = torch.empty(ws, dtype=torch.uint8, device=DEV)
+    out = torch.empty((w.B, w.H_Q, w.d_h), dtype=torch.float32, device=DEV)
+    pkv.cascade_partitions(out, g(w.q[0]), kc, vc, bt, cl, w.max_context_len, w.softmax_scale,
+                           75, workspace=work)
+    torch.cuda.synchronize()
+    assert torch.equal(kc, k0) and torch.equal(vc, v0)
+    pkv.decode_step_cascade(g(w.k_new[0]), g(w.v_new[0]), out, g(w.q[0]), kc, vc, bt, cl,
+                            w.max_context_len, w.softmax_scale, 75, workspace=work)
+    torch.cuda.synchronize()
+    d = _np(w)
+    rk, rv, ref = oracle_step(w, d)
+    assert np.array_equal(as_numpy(kc.cpu()), rk) and np.array_equal(as_numpy(vc.cpu()), rv)
+    assert float(np.max(np.abs(out.cpu().numpy().astype(np.float64) - ref))) <= TOL
