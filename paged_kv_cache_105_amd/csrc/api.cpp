@@ -655,21 +655,40 @@ int pkv_swap_in(void* k_cache, void* v_cache, int kv_dtype, float* k_scale, floa
 
 namespace {
 
-// Split count of a cascade's prefix work: enough waves to cover the chip
-// about once, but at least kMinPrefixBlocks shared blocks per wave -- the
-// prefix waves run beside the longer private-block waves of the same
-// launch, so longer splits cost little, while every split adds a piece per
-// (request, head) that is written and read back by the combine -- and no
-// empty split.
-constexpr int kMinPrefixBlocks = 24;
+// Launch shape of a cascade.  The flat kernel's grid G (sized by occupancy:
+// one workgroup per SIMD for bf16) is shared by the prefix workgroups and the
+// private chunks, so every workgroup is resident from the start: on the
+// shared-prefix batch (64 requests, 75 shared blocks) any grid beyond G cost
+// 8-13% of the kernel time.  The shared blocks are split so that a prefix
+// workgroup walks about as many blocks as a private chunk: the total work,
+// tiles x shared blocks of prefix plus the private blocks, spread over G.
+// The host knows only the longest context, so the private blocks are
+// estimated as 3/4 of B x H_KV x (blocks of the longest context - shared
+// blocks).  Measured on that batch (kernel us, prefix splits / private
+// chunks): 1 / 960: 68.8 (the prefix walks become the longest),
+// 2 / 896: 48.8, 3 / 832: 50.1, 4 / 768: 50.6; 4 / 1024: 51.6.
+struct CascadeShape {
+  int splits;   // prefix splits (no empty split)
+  int chunks;   // private chunks of the balanced split
+};
 
-int cascade_splits(int B, int g, int H_KV, int shared_blocks) {
+CascadeShape cascade_shape(int grid, int B, int g, int H_KV, int shared_blocks, int block_size,
+                           int max_context_len) {
   const long long tiles = (static_cast<long long>(B) * g + 31) / 32 * H_KV;
-  long long want = (1024 + tiles - 1) / tiles;
-  want = std::min<long long>(want, (shared_blocks + kMinPrefixBlocks - 1) / kMinPrefixBlocks);
-  want = std::max<long long>(want, 1);
+  const long long ctx_blocks = (static_cast<long long>(max_context_len) + block_size - 1) / block_size;
+  const long long priv = static_cast<long long>(B) * H_KV *
+                         std::max<long long>(ctx_blocks - shared_blocks, 0) * 3 / 4;
+  const long long per_slot =
+      std::max<long long>((tiles * shared_blocks + priv) / std::max(grid, 1), 1);
+  long long want = (shared_blocks + per_slot - 1) / per_slot;
+  want = std::max<long long>(std::min<long long>(want, shared_blocks), 1);
   const int bps = static_cast<int>((shared_blocks + want - 1) / want);
-  return (shared_blocks + bps - 1) / bps;
+  CascadeShape c;
+  c.splits = (shared_blocks + bps - 1) / bps;
+  const long long prefix_waves = c.splits * tiles;
+  c.chunks = static_cast<int>(std::max<long long>(grid - prefix_waves, grid / 2));
+  c.chunks = std::max(c.chunks, 1);
+  return c;
 }
 
 int cascade_plan(int variant, int B, int H_Q, int H_KV, int d_h, int block_size,
@@ -683,8 +702,11 @@ int cascade_plan(int variant, int B, int H_Q, int H_KV, int d_h, int block_size,
     return PKV_ERR_INVALID_ARG;
   // the cascade launches the flat kernel's cascade variant: size its grid
   // (and the layout) by that kernel's occupancy
-  plan->waves = flat_waves_cached(kv_dtype, H_Q / H_KV, B, true);
-  *splits = cascade_splits(B, H_Q / H_KV, H_KV, shared_blocks);
+  const CascadeShape c =
+      cascade_shape(flat_waves_cached(kv_dtype, H_Q / H_KV, B, true), B, H_Q / H_KV, H_KV,
+                    shared_blocks, block_size, max_context_len);
+  plan->waves = c.chunks;
+  *splits = c.splits;
   *ws = pkv::cascade_layout(B, H_Q, plan->waves, H_Q / H_KV, d_h, *splits).total;
   return PKV_OK;
 }
