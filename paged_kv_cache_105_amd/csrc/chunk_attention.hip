@@ -11,13 +11,17 @@
 // ctx_b - n_b .. ctx_b - 1 (ctx_b = context_lens[b], after the chunk's
 // append); query row query_start[b] + i sits at position ctx_b - n_b + i.
 //
-// Two kernels:
-//   * chunk_mfma_kernel (bf16 queries, bf16 or fp8 caches, d_h 128, 16-slot
-//     blocks): one wave per (tile of 16 NG columns, KV head, request), a
-//     column being one (new token, query head of the group) pair, columns
-//     ordered token-major.  The wave walks blocks 0 .. (its last position) /
-//     16 with the shared MFMA step (mfma_tiles.h); each column masks the
-//     positions after its own.  No split: every wave writes final outputs.
+// Three kernels:
+//   * chunk_mfma_wg_kernel (bf16 queries and caches, d_h 128, 16-slot
+//     blocks): one workgroup of four waves per (tile of 128 columns, KV
+//     head, request), a column being one (new token, query head of the
+//     group) pair, columns ordered token-major.  The workgroup walks blocks
+//     0 .. (its last position) / 16, loading each pair of blocks once into
+//     LDS for all four waves; each column masks the positions after its own.
+//     No split: every wave writes final outputs.
+//   * chunk_mfma_kernel (the same for fp8 caches): one wave per tile of 32
+//     columns, each wave loading its own tiles and using the shared MFMA step
+//     (mfma_tiles.h).
 //   * chunk_generic_kernel (any supported dtype pair, d_h <= 256, any block
 //     size): one wave per (query row, query head); two passes over the
 //     positions (max and sum, then weights and values).  A reference path.
@@ -45,7 +49,7 @@ __device__ __forceinline__ bool chunk_bounds(const DecodeArgs& a, int b, int& qs
 }  // namespace
 
 // ---------------------------------------------------------------------------
-// MFMA kernel
+// One-wave MFMA kernel (fp8 caches)
 // ---------------------------------------------------------------------------
 
 template <int KV, int NG>
@@ -104,6 +108,248 @@ __global__ __launch_bounds__(64, 2) void chunk_mfma_kernel(DecodeArgs a) {
       *reinterpret_cast<f32x4*>(dst + 32 * L.q4 + 8 * ii) = w0 * mul;
       *reinterpret_cast<f32x4*>(dst + 32 * L.q4 + 8 * ii + 4) = w1 * mul;
     }
+  }
+}
+
+
+// ---------------------------------------------------------------------------
+// Workgroup MFMA kernel (bf16 caches): four waves share every K/V tile
+// ---------------------------------------------------------------------------
+//
+// One workgroup of four waves per (tile of 128 columns, KV head, request);
+// wave w holds columns 32w .. 32w + 31 of the tile (two groups of 16), with
+// the score and softmax steps of the one-wave kernel.  The four waves load
+// each pair of blocks together (each thread 16 bytes of each block's K and
+// V), once for all 128 columns, into one of two LDS stages: the loads of
+// pair p + 2 go out after pair p's products and are stored after pair p + 1's,
+// so they have a whole step to arrive.  K is stored in the transposed layout
+// the score products read; V row-major with its 32-byte column groups
+// XOR-swizzled by row, and read as the P.V operand with gfx950's transposing
+// LDS read (ds_read_b64_tr_b16): lane 16q + 4e + j reads the 4 dims
+// 16n + 4j .. + 3 of token q + 4e, and the transpose hands lane 16q + c the
+// dim 16n + c of tokens q, q + 4, q + 8, q + 12 -- the operand of P.V step
+// n, whose accumulator then holds dims 16n + 4q .. 16n + 4q + 3 of column c.
+// So V needs no byte permutes.  Positions past the cached ones are stored as
+// zeros.
+constexpr int kWgWaves = 4;
+constexpr int kWgCols = 16 * 2 * kWgWaves;  // columns per workgroup
+typedef short i16x4v __attribute__((ext_vector_type(4)));
+
+// LDS byte offset of (token t, 32-byte column group k) of a V tile
+__device__ __forceinline__ int v_tile_off(int t, int k) { return (t * 8 + (k ^ (t & 7))) * 32; }
+
+// 16 bytes at byte `off` (< 4096) of the head tile at `tile` (a uniform
+// address): a raw buffer load (descriptor word 3 = 0x00020000: 32-bit data
+// format, no swizzle), so the tile's base stays in scalar registers
+__device__ __forceinline__ u32x4 load_tile16(const char* tile, uint32_t off) {
+  const __amdgpu_buffer_rsrc_t r =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(tile), 0, kBS * kD * 2, 0x00020000);
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
+__device__ __forceinline__ u32x2 lds_read_tr16(const char* p) {
+  const i16x4v r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) i16x4v*)(p));
+  return __builtin_bit_cast(u32x2, r);
+}
+
+__global__ __launch_bounds__(64 * kWgWaves, 2) void chunk_mfma_wg_kernel(DecodeArgs a) {
+  constexpr int NG = 2;
+  // [stage][block of the pair]: K in the score layout, V row-major swizzled
+  __shared__ u32x4 k_lds[2][2][kBS * 16];
+  __shared__ __align__(16) char v_lds[2][2][kBS * kD * 2];
+  const LaneMap L = lane_map();
+  const int wave = threadIdx.x >> 6, tid = threadIdx.x;
+  const int item = xcd_block(blockIdx.x, gridDim.x);
+  const int tile = item % a.chunk_tiles;
+  const int h = (item / a.chunk_tiles) % a.H_KV, b = item / a.chunk_tiles / a.H_KV;
+  int qs0, n_new, ctx;
+  if (!chunk_bounds(a, b, qs0, n_new, ctx)) return;  // uniform over the workgroup
+  const int g = a.g, cols = n_new * g, c0w = tile * kWgCols;
+  if (c0w >= cols) return;                            // uniform over the workgroup
+  const int first = ctx - n_new;
+  // this wave's columns (a wave past the chunk still loads and waits)
+  const int c0 = c0w + 32 * wave;
+  const bool active = c0 < cols;
+  const int c_last = min(c0 + 32, cols) - 1;
+  const int p_first = first + min(c0, cols - 1) / g, p_last = first + c_last / g;
+  const int p_last_wg = first + (min(c0w + kWgCols, cols) - 1) / g;
+  const int nblk = p_last_wg / kBS + 1;               // the workgroup's blocks
+  const int nblk_w = active ? p_last / kBS + 1 : 0;   // the blocks this wave scores
+
+  bf16x8 qop[NG][4];
+  int pcol[NG];
+#pragma unroll
+  for (int G = 0; G < NG; ++G) {
+    const int col = c0 + 16 * G + L.c;
+    pcol[G] = first + min(col, c_last) / g;
+    const uint16_t* qrow = static_cast<const uint16_t*>(a.q) +
+                           (static_cast<size_t>(qs0 + min(col, cols - 1) / g) * a.H_Q + h * g +
+                            min(col, cols - 1) % g) * kD;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (col < cols) v = *reinterpret_cast<const u32x4*>(qrow + 32 * j + 8 * L.q4);
+      qop[G][j] = __builtin_bit_cast(bf16x8, v);
+    }
+  }
+  Acc<NG> acc;
+  acc_init<NG>(acc);
+
+  // loading: thread tid moves 16 bytes (token tid / 16, dims 8 (tid % 16) ..)
+  // of K and of V of both blocks of a pair
+  const int lt = tid >> 4, lc = tid & 15;
+  const int k_wr = lt * 16 + (lc ^ (4 * (lt & 3) + (lt >> 2)));
+  const int v_wr = v_tile_off(lt, lc >> 1) + (lc & 1) * 16;
+  const size_t head_bytes = static_cast<size_t>(kBS) * kD * 2;
+  const size_t blk_bytes = head_bytes * a.H_KV;
+  const char* kbase = static_cast<const char*>(a.k_cache) + h * head_bytes;
+  const char* vbase = static_cast<const char*>(a.v_cache) + h * head_bytes;
+  const uint32_t lane_off = static_cast<uint32_t>(tid) * 16u;
+  const int32_t* row = a.block_table + static_cast<size_t>(b) * a.max_blocks_per_seq;
+  int win0 = 0;
+  int tab = L.lane < nblk ? min(max(row[L.lane], 0), a.num_blocks - 1) : 0;
+  auto block_of = [&](int i) {
+    if (i - win0 >= 64) {  // uniform, at most once per 64 blocks
+      win0 += 64;
+      tab = L.lane + win0 < nblk ? min(max(row[L.lane + win0], 0), a.num_blocks - 1) : 0;
+    }
+    return i < nblk ? __builtin_amdgcn_readlane(tab, i - win0) : 0;
+  };
+  u32x4 rk[2], rv[2];
+  // block addresses are uniform: one scalar base per block, the thread's
+  // 16-byte offset in a vector register
+  auto load_pair = [&](int p) {
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const size_t off = static_cast<size_t>(block_of(2 * p + e)) * blk_bytes;
+      rk[e] = load_tile16(kbase + off, lane_off);
+      rv[e] = load_tile16(vbase + off, lane_off);
+    }
+  };
+  auto store_pair = [&](int p, int st) {
+    if ((2 * p + 2) * kBS > ctx) {  // uniform: the pair has uncached positions
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        if (lt >= ctx - (2 * p + e) * kBS) rk[e] = rv[e] = u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      k_lds[st][e][k_wr] = rk[e];
+      *reinterpret_cast<u32x4*>(&v_lds[st][e][v_wr]) = rv[e];
+    }
+  };
+
+  // score one block of the pair from the shared K tile
+  auto score = [&](const u32x4* kt, int i, float (&s2)[NG][4]) {
+    const int t0 = i * kBS;
+    const int valid = i < nblk ? min(ctx - t0, kBS) : 0;
+    const bool full = valid >= kBS && t0 + kBS - 1 <= p_first;
+    bf16x8 ka[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) ka[j] = __builtin_bit_cast(bf16x8, kt[L.rpos[j]]);
+#pragma unroll
+    for (int G = 0; G < NG; ++G) {
+      f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[j], qop[G][j], sc, 0, 0, 0);
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) s2[G][ii] = sc[ii];
+      if (!full) {
+        const int lim = min(pcol[G] - t0, valid - 1);
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii)
+          if (L.q4 + 4 * ii > lim) s2[G][ii] = -INFINITY;
+      }
+    }
+  };
+
+  const float kscale = a.scale_log2;
+  const int npairs = (nblk + 1) >> 1;
+  // tr-read addresses: lane 16q + 4e + j reads token q + 4e, dims 16n + 4j
+  const int tr_tok = L.q4 + 4 * ((L.lane & 15) >> 2);
+  const int tr_j = L.lane & 3;
+
+  // pair p + 1 is stored after pair p's products (the stage it overwrites
+  // held pair p - 1, which every wave finished before the barrier), and pair
+  // p + 2 is loaded right after: each pair's loads have a whole step to land
+  load_pair(0);
+  store_pair(0, 0);
+  if (npairs > 1) load_pair(1);
+  for (int p = 0; p < npairs; ++p) {
+    const int st = p & 1;
+    __syncthreads();  // stage st holds pair p; stage st ^ 1 is no longer read
+    if (2 * p < nblk_w) {  // uniform per wave: the pair has positions this wave sees
+      float sa[NG][4], sb[NG][4];
+      score(k_lds[st][0], 2 * p, sa);
+      score(k_lds[st][1], 2 * p + 1, sb);
+      bf16x8 ph[NG], pl[NG];
+#pragma unroll
+      for (int G = 0; G < NG; ++G) {
+        const float mxa = fmax_fast(fmax_fast(sa[G][0], sa[G][1]), fmax_fast(sa[G][2], sa[G][3]));
+        const float mxb = fmax_fast(fmax_fast(sb[G][0], sb[G][1]), fmax_fast(sb[G][2], sb[G][3]));
+        const float mx = colmax4(fmax_fast(mxa, mxb) * kscale);
+        if (__any(mx > acc.m[G] + kRescaleSlack)) {
+          const float m_new = fmaxf(acc.m[G], mx);
+          const float alpha = __builtin_amdgcn_exp2f(acc.m[G] - m_new);
+          acc.l[G] *= alpha;
+#pragma unroll
+          for (int nn = 0; nn < 8; ++nn) acc.o[G][nn] *= alpha;
+          acc.m[G] = m_new;
+        }
+        float pr[8];
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+          pr[ii] = __builtin_amdgcn_exp2f(__builtin_fmaf(sa[G][ii], kscale, -acc.m[G]));
+          pr[4 + ii] = __builtin_amdgcn_exp2f(__builtin_fmaf(sb[G][ii], kscale, -acc.m[G]));
+        }
+        acc.l[G] += ((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7]));
+        u32x4 hi, lo;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const uint32_t hh = pack_bf16x2(pr[2 * k], pr[2 * k + 1]);
+          hi[k] = hh;
+          lo[k] = pack_bf16x2(pr[2 * k] - __uint_as_float(hh << 16),
+                              pr[2 * k + 1] - __uint_as_float(hh & 0xffff0000u));
+        }
+        ph[G] = __builtin_bit_cast(bf16x8, hi);
+        pl[G] = __builtin_bit_cast(bf16x8, lo);
+      }
+      const char* va = v_lds[st][0];
+      const char* vb = v_lds[st][1];
+#pragma unroll
+      for (int n = 0; n < 8; ++n) {
+        const int off = v_tile_off(tr_tok, n) + 8 * tr_j;
+        const u32x2 x = lds_read_tr16(va + off), y = lds_read_tr16(vb + off);
+        const bf16x8 v8 = __builtin_bit_cast(bf16x8, u32x4{x.x, x.y, y.x, y.y});
+#pragma unroll
+        for (int G = 0; G < NG; ++G) {
+          acc.o[G][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v8, ph[G], acc.o[G][n], 0, 0, 0);
+          acc.o[G][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v8, pl[G], acc.o[G][n], 0, 0, 0);
+        }
+      }
+    }
+    if (p + 1 < npairs) {
+      store_pair(p + 1, st ^ 1);
+      if (p + 2 < npairs) load_pair(p + 2);
+    }
+  }
+
+  // normalised outputs: lane l holds column 16G + c, dims 16n + 4q .. + 3
+  if (!active) return;
+#pragma unroll
+  for (int G = 0; G < NG; ++G) {
+    float l_tot = acc.l[G] + __shfl_xor(acc.l[G], 16, 64);
+    l_tot += __shfl_xor(l_tot, 32, 64);
+    const int col = c0 + 16 * G + L.c;
+    if (col >= cols) continue;
+    float* dst = a.out + (static_cast<size_t>(qs0 + col / g) * a.H_Q + h * g + col % g) * kD;
+    const float mul = 1.0f / l_tot;
+#pragma unroll
+    for (int n = 0; n < 8; ++n)
+      *reinterpret_cast<f32x4*>(dst + 16 * n + 4 * L.q4) = acc.o[G][n] * mul;
   }
 }
 
@@ -211,9 +457,14 @@ hipError_t launch_chunk_mfma(int kv_dtype, int max_q_len, const DecodeArgs& a,
   DecodeArgs ta = a;
   ta.chunk_tiles = static_cast<int32_t>(tiles);
   const dim3 grid(static_cast<unsigned>(items));
-  if (kv_dtype == DT_BF16)
-    hipLaunchKernelGGL((chunk_mfma_kernel<DT_BF16, kChunkNG>), grid, dim3(64), 0, stream, ta);
-  else
+  if (kv_dtype == DT_BF16) {
+    const long long wtiles = (cols + kWgCols - 1) / kWgCols;
+    const long long witems = wtiles * a.H_KV * a.B;
+    if (witems > 0x7fffffffLL) return hipErrorInvalidValue;
+    ta.chunk_tiles = static_cast<int32_t>(wtiles);
+    hipLaunchKernelGGL(chunk_mfma_wg_kernel, dim3(static_cast<unsigned>(witems)),
+                       dim3(64 * kWgWaves), 0, stream, ta);
+  } else
     hipLaunchKernelGGL((chunk_mfma_kernel<DT_FP8, kChunkNG>), grid, dim3(64), 0, stream, ta);
   return hipGetLastError();
 }
