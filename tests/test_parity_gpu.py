@@ -177,6 +177,8 @@ def _fused_step(w, variant, partition_tokens=0):
     ("fp8_gqa", dict(lens_after=[1, 16, 17, 400, 1025, 3000])),
     ("fp8_mqa", dict(lens_after=[1, 17, 400, 1025])),
     ("llama8b", dict(lens_after=[5, 300, 40000], H_Q=32, H_KV=8)),
+    ("llama8b", dict(lens_after=[1, 16, 17, 32, 33, 600], H_Q=32, H_KV=1)),
+    ("fp8_mha", dict(lens_after=[1, 2, 16, 17, 48, 49, 500])),
 ], ids=lambda x: str(x)[:30])
 def test_decode_step_fused_append(variant, name, kw):
     """pkv_decode_step (the append inside the attention launch where the MFMA
