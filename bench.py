@@ -661,6 +661,8 @@ def main():
                     help="comma-separated decode workloads measured in the same run as "
                          "sub-records (step and kernel figures); empty for none")
     ap.add_argument("--partition", type=int, default=0, help="positions per partition, 0 = default")
+    ap.add_argument("--rest", type=float, default=5.0,
+                    help="seconds the GPU idles before each --also workload is measured")
     ap.add_argument("--rotate", type=int, default=4, help="KV pool copies for cold-cache timing")
     ap.add_argument("--variant", type=int, default=0, help="0 auto, 1 generic, 2 mfma")
     ap.add_argument("--cpu-budget", type=float, default=10.0,
@@ -719,9 +721,16 @@ def main():
     del w, pools
     torch.cuda.empty_cache()
 
-    # the other target workloads, measured in the same run
+    # the other target workloads, measured in the same run.  Each starts from
+    # the rested state the first one starts from: after ~10 s of
+    # full-bandwidth load the chip runs ~4% slower for a few seconds (a
+    # workload measured right after another reads 168-169 us instead of
+    # 161.5-162 us on the 32K batch, whichever order), so the GPU idles
+    # args.rest seconds first, outside every timed region.
     also = {}
     for name in [x for x in args.also.split(",") if x and x != args.workload]:
+        torch.cuda.synchronize()
+        time.sleep(max(args.rest, 0.0))
         sub, w2, p2 = decode_measure(args, name, dev, full=False)
         also[name] = {"us_per_step_per_layer": sub["config"]["us_per_step_per_layer"],
                       "step_gbs": sub["value"],

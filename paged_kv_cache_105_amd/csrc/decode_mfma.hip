@@ -276,7 +276,7 @@ __device__ __forceinline__ int load_window(const DecodeArgs& a, const Cursor& c,
 // have.
 template <int KV, int NG, bool FUSED, bool CASCADE, int HW = 1>
 __global__ __launch_bounds__(64 * HW, 2) void decode_mfma_flat_kernel(DecodeArgs a) {
-  static_assert(HW == 1 || ((HW == 2 || HW == 4) && !CASCADE),
+  static_assert(HW == 1 || ((HW == 2 || HW == 4 || HW == 8) && !CASCADE),
                 "split chunks: two or four waves, no cascade");
   __shared__ u32x4 lds_k_all[HW][kBS * 16];
   // the pieces waves 1 .. HW - 1 leave for the merge: [wave - 1][group][o
@@ -662,21 +662,25 @@ struct KernelPick {
 // bytes for the same per-block chain of dependent products, so with several
 // query heads per KV head the walks are latency bound and more walks per
 // SIMD pay, best as four waves on each of half as many chunks (fewer cut
-// sequences); with one query head per KV head there is little work per
-// block and one wave per chunk at full occupancy streams best; bf16 walks
-// stream best one per SIMD.  Measured on MI355X, kernel us with 1 / 2 / 4
-// waves per chunk: fp8 MQA 40.6 / 37.0 / 34.4, fp8 GQA 159.8 / 152.9 /
-// 152.6, fp8 MHA 568.6 (full occupancy) / - / 582.2, 8B-style bf16 batch
-// 54.5 / 55.6 / 55.4, 32K bf16 161.5 / 164.0 / 162.5.  PKV_FLAT_SPLIT (1, 2
-// or 4) overrides it, for tuning measurements.
+// sequences), and with two head groups per wave (g > 16) as eight waves on
+// a quarter as many, whose 32-head pieces then shrink the combine's work;
+// with one query head per KV head there is little work per block and one
+// wave per chunk at full occupancy streams best; bf16 walks stream best one
+// per SIMD.  Measured on MI355X, kernel us with 1 / 2 / 4 waves per chunk:
+// fp8 MQA 40.6 / 37.0 / 34.4, fp8 GQA 159.8 / 152.9 / 152.6, fp8 MHA 568.6
+// (full occupancy) / - / 582.2, 8B-style bf16 batch 54.5 / 55.6 / 55.4, 32K
+// bf16 161.5 / 164.0 / 162.5; step us with 4 / 8 waves per chunk: fp8 MQA
+// 46.6-47.0 / 45.7-45.9 (the same kernel time), fp8 GQA 166.5-167.8 /
+// 168.7-169.1.  PKV_FLAT_SPLIT (1, 2, 4 or 8; 8 only for fp8 caches with
+// two head groups) overrides it, for tuning measurements.
 int flat_split(int kv_dtype, int g) {
   static const int forced = [] {
     const char* e = std::getenv("PKV_FLAT_SPLIT");
     const int v = e ? std::atoi(e) : 0;
-    return (v == 1 || v == 2 || v == 4) ? v : 0;
+    return (v == 1 || v == 2 || v == 4 || v == 8) ? v : 0;
   }();
-  if (forced) return forced;
-  return kv_dtype == DT_FP8 && g >= 4 ? 4 : 1;
+  if (forced) return forced == 8 && !(kv_dtype == DT_FP8 && g > 16) ? 4 : forced;
+  return kv_dtype == DT_FP8 && g >= 4 ? (g > 16 ? 8 : 4) : 1;
 }
 
 template <int KV, int NG, bool FUSED = false>
@@ -688,6 +692,11 @@ KernelPick mfma_kernel_ptr(bool flat, bool cascade, int split) {
     case 2:
       return {reinterpret_cast<const void*>(&decode_mfma_flat_kernel<KV, NG, FUSED, false, 2>), 2};
     case 4:
+      return {reinterpret_cast<const void*>(&decode_mfma_flat_kernel<KV, NG, FUSED, false, 4>), 4};
+    case 8:  // fp8 caches with two head groups only (flat_split)
+      if constexpr (KV == DT_FP8 && NG == 2 && !FUSED)
+        return {reinterpret_cast<const void*>(&decode_mfma_flat_kernel<KV, NG, false, false, 8>),
+                8};
       return {reinterpret_cast<const void*>(&decode_mfma_flat_kernel<KV, NG, FUSED, false, 4>), 4};
     default:
       return {reinterpret_cast<const void*>(&decode_mfma_flat_kernel<KV, NG, FUSED, false, 1>), 1};
