@@ -664,9 +664,10 @@ namespace {
 // tiles x shared blocks of prefix plus the private blocks, spread over G.
 // The host knows only the longest context, so the private blocks are
 // estimated as 3/4 of B x H_KV x (blocks of the longest context - shared
-// blocks).  Measured on that batch (kernel us, prefix splits / private
-// chunks): 1 / 960: 68.8 (the prefix walks become the longest),
-// 2 / 896: 48.8, 3 / 832: 50.1, 4 / 768: 50.6; 4 / 1024: 51.6.
+// blocks); the prefix takes at most half the grid.  Measured on that batch
+// (kernel us, prefix splits / private chunks): 1 / 960: 68.8 (the prefix
+// walks become the longest), 2 / 896: 48.8, 3 / 832: 50.1, 4 / 768: 50.6;
+// 4 / 1024: 51.6.
 struct CascadeShape {
   int splits;   // prefix splits (no empty split)
   int chunks;   // private chunks of the balanced split
@@ -681,6 +682,9 @@ CascadeShape cascade_shape(int grid, int B, int g, int H_KV, int shared_blocks, 
   const long long per_slot =
       std::max<long long>((tiles * shared_blocks + priv) / std::max(grid, 1), 1);
   long long want = (shared_blocks + per_slot - 1) / per_slot;
+  // at most half the grid for the prefix, so the private chunks keep the
+  // other half and the launch still fits the grid
+  want = std::min<long long>(want, std::max<long long>(grid / 2 / tiles, 1));
   want = std::max<long long>(std::min<long long>(want, shared_blocks), 1);
   const int bps = static_cast<int>((shared_blocks + want - 1) / want);
   CascadeShape c;

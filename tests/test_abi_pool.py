@@ -299,3 +299,30 @@ def test_decode_workspace_size_covers_every_variant():
         assert e.value.name == "invalid_arg"
     finally:
         pkv.set_decode_variant(prev)
+
+
+def test_cascade_plan_sizes_prefix_splits_to_the_private_chunks():
+    # host-only: the cascade's prefix splits follow the estimated private
+    # work, leave at least half the grid to the private chunks and never
+    # exceed the shared blocks.  Without a device (and on MI355X with bf16
+    # caches) the flat grid is 1,024 workgroups.
+    def splits(B, H_Q, H_KV, max_ctx, shared):
+        return pkv.cascade_plan(B, H_Q, H_KV, 128, 16, max_ctx, shared)[0]
+
+    # the shared-prefix batch: 64 requests, 75 shared blocks, longest context
+    # 1,200 + 600 + 900 + 1: two splits of 38 and 37 blocks (measured best)
+    assert splits(64, 32, 8, 2701, 75) == 2
+    # private parts of one block: the prefix work dominates; capped at half
+    # the grid (8 splits x 64 column tiles)
+    assert splits(64, 32, 8, 1216, 75) == 8
+    # few requests: the prefix is cut finer, down to one block per split
+    assert splits(6, 32, 8, 2701, 75) == 25
+    assert splits(3, 32, 1, 2701, 75) == 75
+    # so many requests that the column tiles alone exceed half the grid
+    assert splits(4096, 32, 8, 2000, 75) == 1
+    for B, H_Q, H_KV, max_ctx, shared in [(64, 32, 8, 2701, 75), (7, 32, 8, 2000, 4),
+                                          (5, 8, 8, 700, 30), (64, 32, 8, 1216, 75)]:
+        s = splits(B, H_Q, H_KV, max_ctx, shared)
+        assert 1 <= s <= shared
+        tiles = -(-B * (H_Q // H_KV) // 32) * H_KV
+        assert s == 1 or s * tiles <= 512
