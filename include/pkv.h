@@ -318,9 +318,11 @@ int pkv_paged_decode_attention(float* out, const void* q, int q_dtype, const voi
  * query dtype) followed by pkv_paged_decode_attention, same arguments and
  * results (the pools end up byte for byte as after pkv_kv_append; k_cache
  * and v_cache are written).  Where the MFMA kernels run on a bf16 cache
- * with H_Q / H_KV <= 16, the append is done inside the attention launch by the wave that reads the
- * request's last block, which uses the new row from registers (one launch
- * fewer); other cases launch the append kernel first. */
+ * with H_Q / H_KV <= 16, or on an fp8 cache with H_Q / H_KV > 16 and the
+ * balanced split, the append is done inside the attention launch by the
+ * wave that reads the request's last block, which uses the new row from
+ * registers (one launch fewer); other cases launch the append kernel
+ * first. */
 int pkv_decode_step(const void* k_new, const void* v_new, float* out, const void* q, int q_dtype,
                     void* k_cache, void* v_cache, int kv_dtype, const float* k_scale,
                     const float* v_scale, const int32_t* block_table, int32_t max_blocks_per_seq,

@@ -36,7 +36,7 @@ hipError_t launch_decode_generic(int q_dtype, int kv_dtype, const DecodeArgs& a,
                                  hipStream_t stream);
 size_t generic_lds_bytes(int g, int d_h, int partition_tokens);
 bool mfma_supports(int q_dtype, int kv_dtype, int d_h, int block_size, int g);
-bool mfma_fuses_append(int kv_dtype, int g);
+bool mfma_fuses_append(int kv_dtype, int g, bool flat, bool cascade);
 int mfma_flat_waves(int kv_dtype, int g, int B, bool cascade);
 hipError_t launch_decode_mfma(int kv_dtype, bool flat, int waves, const DecodeArgs& a,
                               hipStream_t stream);
@@ -443,7 +443,7 @@ int decode_launch(int variant, Plan* plan_out, const void* k_new, const void* v_
   a.scale_log2 = softmax_scale * pkv::kLog2e;
   a.k_new = k_new;
   a.v_new = v_new;
-  if (k_new && (!pkv::mfma_fuses_append(kv_dtype, H_Q / H_KV) ||
+  if (k_new && (!pkv::mfma_fuses_append(kv_dtype, H_Q / H_KV, plan.kernel == K_MFMA_FLAT, false) ||
                 (plan.kernel != K_MFMA_FLAT && plan.kernel != K_MFMA_PARTITION)))
     return PKV_ERR_UNSUPPORTED;
 
@@ -550,7 +550,8 @@ int pkv_decode_step(const void* k_new, const void* v_new, float* out, const void
   if (reinterpret_cast<uintptr_t>(workspace) & 15) return PKV_ERR_INVALID_ARG;
   const bool aligned =
       ((reinterpret_cast<uintptr_t>(k_new) | reinterpret_cast<uintptr_t>(v_new)) & 15) == 0;
-  const bool fused = aligned && pkv::mfma_fuses_append(kv_dtype, H_Q / H_KV) &&
+  const bool fused = aligned &&
+                     pkv::mfma_fuses_append(kv_dtype, H_Q / H_KV, plan.kernel == K_MFMA_FLAT, false) &&
                      (plan.kernel == K_MFMA_FLAT || plan.kernel == K_MFMA_PARTITION);
   if (!fused) {
     st = pkv_kv_append(k_new, v_new, q_dtype, k_cache, v_cache, kv_dtype, k_scale, v_scale,
@@ -768,7 +769,7 @@ int cascade_step(const void* k_new, const void* v_new, float* out, const void* q
   const hipStream_t s = static_cast<hipStream_t>(stream);
   const bool fused =
       k_new && ((reinterpret_cast<uintptr_t>(k_new) | reinterpret_cast<uintptr_t>(v_new)) & 15) == 0 &&
-      pkv::mfma_fuses_append(kv_dtype, H_Q / H_KV);
+      pkv::mfma_fuses_append(kv_dtype, H_Q / H_KV, true, true);
   if (k_new && !fused) {
     st = pkv_kv_append(k_new, v_new, q_dtype, k_cache, v_cache, kv_dtype, k_scale, v_scale,
                        block_table, max_blocks_per_seq, context_lens, B, H_KV, d_h, block_size,

@@ -20,6 +20,7 @@
 // one the library picks for batches up to 8192 requests.
 
 #include <cstdlib>
+#include <type_traits>
 
 #include "cascade_prefix.h"
 #include "mfma_tiles.h"
@@ -205,6 +206,50 @@ __device__ __forceinline__ void new_row_load(const DecodeArgs& a, const LaneMap&
   const size_t src = (static_cast<size_t>(b) * a.H_KV + h) * kD + 8 * L.c;
   nr.k = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.k_new) + src);
   nr.v = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.v_new) + src);
+}
+
+// fp8 caches: the row arrives in bf16 and is stored as the E4M3 codes of
+// fp32(x) / scale with the scale its block already has -- the stored form of
+// pkv_kv_append (page 2 "KV Cache Explained", "What changes when you use FP8
+// KV": one byte per element plus scales).  The 256 values of the row (K,
+// then V) are spread over the wave, 4 per lane: lane j < 32 holds K dims
+// 4j .. 4j + 3, lane 32 + j the same dims of V.  Nothing else is read
+// early: the block's id and its two scales are in the walk's registers when
+// it reaches the block, so the codes, the store and the substitution all
+// happen there.
+struct NewRowFp8 {
+  int blk;   // the row's block within the sequence, -1: none in this wave
+  int slot;
+  u32x2 x;   // this lane's 4 bf16 values
+};
+template <int KV>
+using NewRowOf = std::conditional_t<KV == DT_FP8, NewRowFp8, NewRow>;
+
+__device__ __forceinline__ void new_row_place(const DecodeArgs& a, const LaneMap&, const_i32p,
+                                              int, int, int n_raw, int jb, int je,
+                                              NewRowFp8& nr) {
+  nr.blk = -1;
+  nr.slot = 0;
+  if (n_raw < 1 || n_raw > a.max_blocks_per_seq * kBS) return;
+  const int jn = (n_raw - 1) / kBS;
+  if (jn < jb || jn >= je) return;
+  nr.blk = jn;
+  nr.slot = (n_raw - 1) % kBS;
+}
+__device__ __forceinline__ void new_row_load(const DecodeArgs& a, const LaneMap& L, int b, int h,
+                                             NewRowFp8& nr) {
+  const size_t src = (static_cast<size_t>(b) * a.H_KV + h) * kD + 4 * (L.lane & 31);
+  const void* row = L.lane < 32 ? a.k_new : a.v_new;
+  nr.x = *reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(row) + src);
+}
+
+// 4 bf16 values (dims 2k, 2k + 1 in word k) -> their E4M3 codes of
+// fp32(x) / s, byte j = the j-th value: the same division (IEEE, correctly
+// rounded) and encoder as pkv_kv_append, so the stored bytes are the same.
+__device__ __forceinline__ uint32_t encode4(const u32x2& x, float s) {
+  const uint32_t c0 = f32_to_e4m3(bf16_lo(x.x) / s), c1 = f32_to_e4m3(bf16_hi(x.x) / s);
+  const uint32_t c2 = f32_to_e4m3(bf16_lo(x.y) / s), c3 = f32_to_e4m3(bf16_hi(x.y) / s);
+  return c0 | (c1 << 8) | (c2 << 16) | (c3 << 24);
 }
 
 // Where the walk is: sequence (b, h) with nb blocks (after any skipped
@@ -446,7 +491,7 @@ __global__ __launch_bounds__(64 * HW, 2) void decode_mfma_flat_kernel(DecodeArgs
   int n0 = min(n_raw0, cap * kBS);
   bf16x8 qop[NG][4];
   load_q<NG>(a, L, cur.b, cur.h, qop);
-  NewRow nr;
+  NewRowOf<KV> nr;
   if constexpr (FUSED) {
     int jb, je;
     seg_bounds(cur, jb, je);
@@ -497,7 +542,32 @@ __global__ __launch_bounds__(64 * HW, 2) void decode_mfma_flat_kernel(DecodeArgs
         for (int G = 0; G < NG; ++G) lim[G] = valid - 1;
         if constexpr (FUSED) {
           if (jb + i == nr.blk) {  // uniform: the block that holds the new row
-            if (L.q4 == (nr.slot & 3)) {
+            if constexpr (KV == DT_FP8) {
+              // the block's id (its table entry) and scales, as the walk loaded them
+              const int p = i < c.nblk ? __builtin_amdgcn_readlane(win, i) : -1;
+              if (p >= 0 && p < a.num_blocks) {
+                const uint32_t code =
+                    encode4(nr.x, L.lane < 32 ? kbuf[u].scale : vbuf[u].scale);
+                const size_t dst =
+                    ((static_cast<size_t>(p) * HKV + c.h) * kBS + nr.slot) * kD + 4 * (L.lane & 31);
+                void* pool = const_cast<void*>(L.lane < 32 ? a.k_cache : a.v_cache);
+                *reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(pool) + dst) = code;
+                // lane (q, c) holds dims 8c .. 8c + 7: the codes of lanes 2c, 2c + 1
+                const u32x2 kw = {static_cast<uint32_t>(__shfl(code, 2 * L.c, 64)),
+                                  static_cast<uint32_t>(__shfl(code, 2 * L.c + 1, 64))};
+                const u32x2 vw = {static_cast<uint32_t>(__shfl(code, 32 + 2 * L.c, 64)),
+                                  static_cast<uint32_t>(__shfl(code, 33 + 2 * L.c, 64))};
+                if (L.q4 == (nr.slot & 3)) {
+#pragma unroll
+                  for (int s = 0; s < 4; ++s) {
+                    if (s == (nr.slot >> 2)) {
+                      kbuf[u].w[s] = kw;
+                      vbuf[u].w[s] = vw;
+                    }
+                  }
+                }
+              }
+            } else if (L.q4 == (nr.slot & 3)) {
               *nr.k_dst = nr.k;
               *nr.v_dst = nr.v;
 #pragma unroll
@@ -633,15 +703,20 @@ __global__ __launch_bounds__(64 * HW, 2) void decode_mfma_flat_kernel(DecodeArgs
   }
 }
 
-// The fused append keeps the new row in registers for the whole walk: with
+// The fused append keeps the new row in registers for the whole walk.  With
 // bf16 caches and one head group that fits (the bf16 kernel runs one wave
-// per SIMD anyway).  For fp8 caches the row is quantised with its block's
-// scale, which the walk has only when it reaches the block: done there, the
-// division, encoding and store at every sequence's last block cost the fp8
-// walk more than the append launch they save (measured on MI355X: fp8 GQA
-// step 175 vs 174 us, fp8 MHA 643 vs 588 us), so fp8 and two head groups
-// launch the append kernel first.
-bool mfma_fuses_append(int kv_dtype, int g) { return kv_dtype == DT_BF16 && g <= 16; }
+// per SIMD anyway), in every launch shape.  fp8 rows are encoded when the
+// walk reaches their block, 4 values per lane; that pays where the walks are
+// long and latency bound, the flat walk with two head groups per wave (fp8
+// MQA: one sequence per request, 32 query heads on it), without a cascade.
+// Measured on MI355X, step us with the append fused / launched first: fp8
+// MQA 45.0-45.6 / 47.0-47.6; fp8 GQA (one head group, four waves per chunk)
+// 170.0-171.2 / 169.1-170.6, no gain; fp8 MHA would lose a wave per SIMD
+// (171 instead of 155 registers: two waves instead of three).
+bool mfma_fuses_append(int kv_dtype, int g, bool flat, bool cascade) {
+  if (kv_dtype == DT_BF16) return g <= 16;
+  return kv_dtype == DT_FP8 && g > 16 && flat && !cascade;
+}
 
 bool mfma_supports(int q_dtype, int kv_dtype, int d_h, int block_size, int g) {
   return q_dtype == DT_BF16 && (kv_dtype == DT_BF16 || kv_dtype == DT_FP8) && d_h == kD &&
@@ -685,21 +760,42 @@ int flat_split(int kv_dtype, int g) {
 
 template <int KV, int NG, bool FUSED = false>
 KernelPick mfma_kernel_ptr(bool flat, bool cascade, int split) {
-  if (!flat) return {reinterpret_cast<const void*>(&decode_mfma_kernel<KV, NG, kDepth, FUSED>), 1};
-  if (cascade)
-    return {reinterpret_cast<const void*>(&decode_mfma_flat_kernel<KV, NG, FUSED, true>), 1};
-  switch (split) {
-    case 2:
-      return {reinterpret_cast<const void*>(&decode_mfma_flat_kernel<KV, NG, FUSED, false, 2>), 2};
-    case 4:
-      return {reinterpret_cast<const void*>(&decode_mfma_flat_kernel<KV, NG, FUSED, false, 4>), 4};
-    case 8:  // fp8 caches with two head groups only (flat_split)
-      if constexpr (KV == DT_FP8 && NG == 2 && !FUSED)
-        return {reinterpret_cast<const void*>(&decode_mfma_flat_kernel<KV, NG, false, false, 8>),
-                8};
-      return {reinterpret_cast<const void*>(&decode_mfma_flat_kernel<KV, NG, FUSED, false, 4>), 4};
-    default:
-      return {reinterpret_cast<const void*>(&decode_mfma_flat_kernel<KV, NG, FUSED, false, 1>), 1};
+  if constexpr (KV == DT_FP8 && FUSED) {
+    // the flat walk without a cascade only (mfma_fuses_append)
+    (void)flat;
+    (void)cascade;
+    switch (split) {
+      case 2:
+        return {reinterpret_cast<const void*>(&decode_mfma_flat_kernel<KV, NG, true, false, 2>), 2};
+      case 4:
+        return {reinterpret_cast<const void*>(&decode_mfma_flat_kernel<KV, NG, true, false, 4>), 4};
+      case 8:
+        return {reinterpret_cast<const void*>(&decode_mfma_flat_kernel<KV, NG, true, false, 8>), 8};
+      default:
+        return {reinterpret_cast<const void*>(&decode_mfma_flat_kernel<KV, NG, true, false, 1>), 1};
+    }
+  } else {
+    if (!flat)
+      return {reinterpret_cast<const void*>(&decode_mfma_kernel<KV, NG, kDepth, FUSED>), 1};
+    if (cascade)
+      return {reinterpret_cast<const void*>(&decode_mfma_flat_kernel<KV, NG, FUSED, true>), 1};
+    switch (split) {
+      case 2:
+        return {reinterpret_cast<const void*>(&decode_mfma_flat_kernel<KV, NG, FUSED, false, 2>),
+                2};
+      case 4:
+        return {reinterpret_cast<const void*>(&decode_mfma_flat_kernel<KV, NG, FUSED, false, 4>),
+                4};
+      case 8:  // fp8 caches with two head groups only (flat_split)
+        if constexpr (KV == DT_FP8 && NG == 2)
+          return {reinterpret_cast<const void*>(&decode_mfma_flat_kernel<KV, NG, FUSED, false, 8>),
+                  8};
+        return {reinterpret_cast<const void*>(&decode_mfma_flat_kernel<KV, NG, FUSED, false, 4>),
+                4};
+      default:
+        return {reinterpret_cast<const void*>(&decode_mfma_flat_kernel<KV, NG, FUSED, false, 1>),
+                1};
+    }
   }
 }
 
@@ -713,6 +809,7 @@ KernelPick pick_kernel(int kv_dtype, int g, bool flat, bool fused, bool cascade)
     return two ? mfma_kernel_ptr<DT_BF16, 2>(flat, cascade, split)
                : mfma_kernel_ptr<DT_BF16, 1>(flat, cascade, split);
   }
+  if (fused && two && flat && !cascade) return mfma_kernel_ptr<DT_FP8, 2, true>(flat, cascade, split);
   return two ? mfma_kernel_ptr<DT_FP8, 2>(flat, cascade, split)
              : mfma_kernel_ptr<DT_FP8, 1>(flat, cascade, split);
 }
@@ -732,7 +829,8 @@ KernelPick pick_kernel(int kv_dtype, int g, bool flat, bool fused, bool cascade)
 int mfma_flat_waves(int kv_dtype, int g, int B, bool cascade) {
   // the occupancy of the variant with the fused append where one exists
   // (the step launches it; it needs at least the registers of the other)
-  const KernelPick k = pick_kernel(kv_dtype, g, true, mfma_fuses_append(kv_dtype, g), cascade);
+  const KernelPick k =
+      pick_kernel(kv_dtype, g, true, mfma_fuses_append(kv_dtype, g, true, cascade), cascade);
   int dev = 0, cus = 0, per_cu = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||

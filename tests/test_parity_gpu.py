@@ -176,6 +176,7 @@ def _fused_step(w, variant, partition_tokens=0):
     ("llama8b", dict(lens_after=[1, 16, 17, 31, 32, 33, 600, 2049], H_Q=32, H_KV=8)),
     ("fp8_gqa", dict(lens_after=[1, 16, 17, 400, 1025, 3000])),
     ("fp8_mqa", dict(lens_after=[1, 17, 400, 1025])),
+    ("fp8_mqa", dict(lens_after=[2, 7, 12, 16, 33, 90, 4100])),
     ("llama8b", dict(lens_after=[5, 300, 40000], H_Q=32, H_KV=8)),
     ("llama8b", dict(lens_after=[1, 16, 17, 32, 33, 600], H_Q=32, H_KV=1)),
     ("fp8_mha", dict(lens_after=[1, 2, 16, 17, 48, 49, 500])),
@@ -361,13 +362,16 @@ class _Override:
 
 
 @pytest.mark.parametrize("variant", VARIANTS, ids=VIDS)
-def test_out_of_range_device_values_stay_contained(variant):
+@pytest.mark.parametrize("name,H_KV", [("llama8b", 8), ("fp8_mqa", 1)])
+def test_out_of_range_device_values_stay_contained(variant, name, H_KV):
     # Device-side values are trusted but never followed outside the caller's
     # buffers: a length of 0, -5 or beyond the table row, and block ids past
     # the pool or negative, only make that request's result unspecified.  The
     # other requests still match the oracle, and none of them is disturbed.
+    # Both decode steps whose append runs inside the attention launch: bf16
+    # with one head group, fp8 with two.
     lens = [5, 300, 900, 17, 2000, 64, 33]
-    w = make_workload("llama8b", lens_after=lens, H_Q=32, H_KV=8)
+    w = make_workload(name, lens_after=lens, H_Q=32, H_KV=H_KV)
     good = [0, 2, 4]
     _, _, ref = oracle_step(w, _np(w), requests=good)
     cl = w.context_lens.clone()
@@ -378,9 +382,11 @@ def test_out_of_range_device_values_stay_contained(variant):
     # pools: only requests with a valid length and a valid last block (0, 2,
     # 4 and 5) get their row; every other byte stays as it was
     sel = [0, 2, 4, 5]
+    sc = lambda x: as_numpy(x[0]) if x else None
     rk, rv = paged.append(as_numpy(w.k_cache[0]), as_numpy(w.v_cache[0]), w.kv_dtype,
                           as_numpy(w.k_new[0])[sel], as_numpy(w.v_new[0])[sel], w.q_dtype,
-                          as_numpy(bt)[sel], as_numpy(cl)[sel], w.block_size)
+                          as_numpy(bt)[sel], as_numpy(cl)[sel], w.block_size, sc(w.k_scale),
+                          sc(w.v_scale))
     # the append kernel + attention, then the decode step (whose MFMA kernels
     # do the append inside the launch)
     for run in (lambda: gpu_step(bad, variant=variant), lambda: _fused_step(bad, variant)):

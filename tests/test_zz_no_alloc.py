@@ -61,9 +61,9 @@ def _oracle(w, requests):
                              inplace=True)[2]
 
 
-# first call, then a smaller second one: the bench's 8B-style batch (append
-# fused into the attention launch), and fp8 with 32 query heads per KV head
-# (separate append kernel, two head groups per wave)
+# first call, then a smaller second one: the bench's 8B-style batch and fp8
+# with 32 query heads per KV head (two head groups per wave), both with the
+# append inside the attention launch
 PAIRS = {
     "bf16": [("llama8b", {}), ("llama8b", dict(lens_after=[40, 700, 17], H_Q=8, H_KV=2))],
     "fp8": [("fp8_mqa", dict(B=24)), ("fp8_mqa", dict(lens_after=[1, 16, 300, 2049]))],
