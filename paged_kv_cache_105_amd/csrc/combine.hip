@@ -31,7 +31,15 @@ namespace pkv {
 
 namespace {
 
-constexpr int kUnroll = 8;
+// Loads of kUnroll iterations go out before any is used.  Measured on
+// MI355X, combine trace us with 8 / 4 / 2: 8B-style batch 5.24 / 4.76 /
+// 4.76, fp8 MQA 7.88 / 7.20 / 6.92, fp8 GQA 8.24 / 7.44 / 6.80, 32K
+// contexts (17 pieces per sequence) 5.28 / 5.40 / 5.92: unused load slots
+// cost instructions in every one of the many waves, too few starve the
+// waves with many pieces.  (Choosing 2, 4 or 8 per wave from its piece
+// count was slower still on fp8 MQA and 32K: the kernel with three copies of
+// the loop ran 8.04 and 6.76 us.)
+constexpr int kUnroll = 4;
 
 template <int VW>
 struct VecT;
