@@ -52,11 +52,14 @@ struct VecT<4> {
   typedef float type __attribute__((ext_vector_type(4)));
 };
 
-// merge (m2, l2) into (m, l): both are (max, sum of 2^(s - max)) of a set
+// merge (m2, l2) into (m, l): both are (max, sum of 2^(s - max)) of a set.
+// The exponentials here have arguments <= 0 and results in (0, 1]; the
+// hardware instruction is used directly (the library form adds steps for
+// results below 2^-126, whose share of any sum is below 2^-126 as well).
 __device__ inline void lse_merge(float& m, float& l, float m2, float l2) {
   const float mn = fmaxf(m, m2);
-  const float a = (m == mn) ? 1.f : exp2f(m - mn);     // also covers m = m2 = -inf
-  const float b = (m2 == mn) ? 1.f : exp2f(m2 - mn);
+  const float a = (m == mn) ? 1.f : __builtin_amdgcn_exp2f(m - mn);  // also covers m = m2 = -inf
+  const float b = (m2 == mn) ? 1.f : __builtin_amdgcn_exp2f(m2 - mn);
   l = l * a + l2 * b;
   m = mn;
 }
@@ -215,7 +218,7 @@ __global__ __launch_bounds__(64) void combine_kernel(float* __restrict__ out,
   for (int k0 = 0; k0 < P; k0 += 64) {
     const int kn = min(64, P - k0);
     const float mk = (k0 == 0) ? m_own : (lane < kn ? ml_at(k0 + lane)[0] : -INFINITY);
-    const float w = lane < kn ? exp2f(mk - M) * inv : 0.f;
+    const float w = lane < kn ? __builtin_amdgcn_exp2f(mk - M) * inv : 0.f;
     const int iters = (kn + PPI - 1) / PPI;
     for (int i0 = 0; i0 < iters; i0 += kUnroll) {
       Vec x[kUnroll][R];
