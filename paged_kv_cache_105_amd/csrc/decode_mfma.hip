@@ -180,54 +180,40 @@ __global__ __launch_bounds__(64, 2) void decode_mfma_kernel(DecodeArgs a) {
 
 typedef const __attribute__((address_space(4))) int32_t* const_i32p;
 
-// The fused append, split for the streaming walk: where the new row goes
-// (from the request's raw length and one table entry, both read through the
-// scalar cache) and, issued separately and early, the row's K and V.  The
-// rules are those of load_new_row: nothing is appended for a length or block
-// id out of range, or when the wave's blocks [jb, je) miss the row's block.
-__device__ __forceinline__ void new_row_place(const DecodeArgs& a, const LaneMap& L,
-                                              const_i32p table, int b, int h, int n_raw,
-                                              int jb, int je, NewRow& nr) {
-  nr.blk = -1;
-  nr.slot = 0;
-  if (n_raw < 1 || n_raw > a.max_blocks_per_seq * kBS) return;
-  const int jn = (n_raw - 1) / kBS;
-  if (jn < jb || jn >= je) return;
-  const int p = table[static_cast<size_t>(b) * a.max_blocks_per_seq + jn];
-  if (p < 0 || p >= a.num_blocks) return;
-  nr.blk = jn;
-  nr.slot = (n_raw - 1) % kBS;
-  const size_t dst = ((static_cast<size_t>(p) * a.H_KV + h) * kBS + nr.slot) * kD + 8 * L.c;
-  nr.k_dst = reinterpret_cast<u32x4*>(static_cast<uint16_t*>(const_cast<void*>(a.k_cache)) + dst);
-  nr.v_dst = reinterpret_cast<u32x4*>(static_cast<uint16_t*>(const_cast<void*>(a.v_cache)) + dst);
-}
-__device__ __forceinline__ void new_row_load(const DecodeArgs& a, const LaneMap& L, int b, int h,
-                                             NewRow& nr) {
-  const size_t src = (static_cast<size_t>(b) * a.H_KV + h) * kD + 8 * L.c;
-  nr.k = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.k_new) + src);
-  nr.v = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.v_new) + src);
-}
-
+// The fused append, split for the streaming walk.  When the wave starts a
+// sequence it works out whether the request's newest position falls in its
+// blocks (from the raw length alone: nothing is appended for a length out of
+// range, or when the wave's blocks [jb, je) miss the row's block) and loads
+// the row's K and V, early.  Nothing else is read then: when the walk reaches
+// that block, the block's id is in the table window it walks with (a row is
+// appended only if that id is inside the pool, the rule of pkv_kv_append),
+// so the store and the substitution into the loaded tile happen there.
+//
+// bf16 caches: lane (q, c) holds dims 8c .. 8c + 7 of both rows, the part of
+// the slot's row it loads from the tile when q == slot % 4.
+struct NewRowBf16 {
+  int blk;   // the row's block within the sequence, -1: none in this wave
+  int slot;
+  u32x4 k, v;
+};
 // fp8 caches: the row arrives in bf16 and is stored as the E4M3 codes of
 // fp32(x) / scale with the scale its block already has -- the stored form of
 // pkv_kv_append (page 2 "KV Cache Explained", "What changes when you use FP8
 // KV": one byte per element plus scales).  The 256 values of the row (K,
 // then V) are spread over the wave, 4 per lane: lane j < 32 holds K dims
-// 4j .. 4j + 3, lane 32 + j the same dims of V.  Nothing else is read
-// early: the block's id and its two scales are in the walk's registers when
-// it reaches the block, so the codes, the store and the substitution all
-// happen there.
+// 4j .. 4j + 3, lane 32 + j the same dims of V.  The block's two scales come
+// with its tile.
 struct NewRowFp8 {
-  int blk;   // the row's block within the sequence, -1: none in this wave
+  int blk;
   int slot;
   u32x2 x;   // this lane's 4 bf16 values
 };
 template <int KV>
-using NewRowOf = std::conditional_t<KV == DT_FP8, NewRowFp8, NewRow>;
+using NewRowOf = std::conditional_t<KV == DT_FP8, NewRowFp8, NewRowBf16>;
 
-__device__ __forceinline__ void new_row_place(const DecodeArgs& a, const LaneMap&, const_i32p,
-                                              int, int, int n_raw, int jb, int je,
-                                              NewRowFp8& nr) {
+template <class NR>
+__device__ __forceinline__ void new_row_place(const DecodeArgs& a, int n_raw, int jb, int je,
+                                              NR& nr) {
   nr.blk = -1;
   nr.slot = 0;
   if (n_raw < 1 || n_raw > a.max_blocks_per_seq * kBS) return;
@@ -235,6 +221,12 @@ __device__ __forceinline__ void new_row_place(const DecodeArgs& a, const LaneMap
   if (jn < jb || jn >= je) return;
   nr.blk = jn;
   nr.slot = (n_raw - 1) % kBS;
+}
+__device__ __forceinline__ void new_row_load(const DecodeArgs& a, const LaneMap& L, int b, int h,
+                                             NewRowBf16& nr) {
+  const size_t src = (static_cast<size_t>(b) * a.H_KV + h) * kD + 8 * L.c;
+  nr.k = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.k_new) + src);
+  nr.v = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.v_new) + src);
 }
 __device__ __forceinline__ void new_row_load(const DecodeArgs& a, const LaneMap& L, int b, int h,
                                              NewRowFp8& nr) {
@@ -495,7 +487,7 @@ __global__ __launch_bounds__(64 * HW, 2) void decode_mfma_flat_kernel(DecodeArgs
   if constexpr (FUSED) {
     int jb, je;
     seg_bounds(cur, jb, je);
-    new_row_place(a, L, table, cur.b, cur.h, n_raw0, jb, je, nr);
+    new_row_place(a, n_raw0, jb, je, nr);
     new_row_load(a, L, cur.b, cur.h, nr);
   }
   issue(kbuf[0], vbuf[0], __builtin_amdgcn_readlane(win0, 0), cur.h);
@@ -542,16 +534,17 @@ __global__ __launch_bounds__(64 * HW, 2) void decode_mfma_flat_kernel(DecodeArgs
         for (int G = 0; G < NG; ++G) lim[G] = valid - 1;
         if constexpr (FUSED) {
           if (jb + i == nr.blk) {  // uniform: the block that holds the new row
-            if constexpr (KV == DT_FP8) {
-              // the block's id (its table entry) and scales, as the walk loaded them
-              const int p = i < c.nblk ? __builtin_amdgcn_readlane(win, i) : -1;
-              if (p >= 0 && p < a.num_blocks) {
+            // its id, from the window the walk loads it with (and, for fp8,
+            // its scales, loaded with the tile)
+            const int p = i < c.nblk ? __builtin_amdgcn_readlane(win, i) : -1;
+            if (p >= 0 && p < a.num_blocks) {
+              const size_t row0 = ((static_cast<size_t>(p) * HKV + c.h) * kBS + nr.slot) * kD;
+              if constexpr (KV == DT_FP8) {
                 const uint32_t code =
                     encode4(nr.x, L.lane < 32 ? kbuf[u].scale : vbuf[u].scale);
-                const size_t dst =
-                    ((static_cast<size_t>(p) * HKV + c.h) * kBS + nr.slot) * kD + 4 * (L.lane & 31);
                 void* pool = const_cast<void*>(L.lane < 32 ? a.k_cache : a.v_cache);
-                *reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(pool) + dst) = code;
+                *reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(pool) + row0 +
+                                             4 * (L.lane & 31)) = code;
                 // lane (q, c) holds dims 8c .. 8c + 7: the codes of lanes 2c, 2c + 1
                 const u32x2 kw = {static_cast<uint32_t>(__shfl(code, 2 * L.c, 64)),
                                   static_cast<uint32_t>(__shfl(code, 2 * L.c + 1, 64))};
@@ -566,15 +559,18 @@ __global__ __launch_bounds__(64 * HW, 2) void decode_mfma_flat_kernel(DecodeArgs
                     }
                   }
                 }
-              }
-            } else if (L.q4 == (nr.slot & 3)) {
-              *nr.k_dst = nr.k;
-              *nr.v_dst = nr.v;
+              } else if (L.q4 == (nr.slot & 3)) {
+                const size_t d = row0 + 8 * L.c;
+                *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(const_cast<void*>(a.k_cache)) + d) =
+                    nr.k;
+                *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(const_cast<void*>(a.v_cache)) + d) =
+                    nr.v;
 #pragma unroll
-              for (int s = 0; s < 4; ++s) {
-                if (s == (nr.slot >> 2)) {
-                  kbuf[u].w[s] = nr.k;
-                  vbuf[u].w[s] = nr.v;
+                for (int s = 0; s < 4; ++s) {
+                  if (s == (nr.slot >> 2)) {
+                    kbuf[u].w[s] = nr.k;
+                    vbuf[u].w[s] = nr.v;
+                  }
                 }
               }
             }
@@ -652,7 +648,7 @@ __global__ __launch_bounds__(64 * HW, 2) void decode_mfma_flat_kernel(DecodeArgs
         if constexpr (FUSED) {
           int jb2, je2;
           seg_bounds(nxt, jb2, je2);
-          new_row_place(a, L, table, nxt.b, nxt.h, n_raw_nxt, jb2, je2, nr);
+          new_row_place(a, n_raw_nxt, jb2, je2, nr);
         }
       }
     }
