@@ -612,6 +612,27 @@ def test_full_size_sampled(name, req):
     assert np.all(np.isfinite(out))
 
 
+@pytest.mark.parametrize("name,req", [("llama8b", None), ("long32k", [0, 7]),
+                                      ("fp8_mqa", [1, 64, 126]), ("fp8_gqa", [0, 127])])
+def test_full_size_decode_step(name, req):
+    # pkv_decode_step at the measured sizes, the call the benchmark times (the
+    # append inside the attention launch for the 8B-style and 32K batches and
+    # fp8 MQA, the append kernel first for fp8 GQA): pools bit-exact, outputs
+    # within tolerance (all requests, or a sample), and every output bitwise
+    # equal to the separate append + attention calls
+    w = make_workload(name)
+    _log(f"{name} full decode step: B={w.B} max_len={w.max_context_len}")
+    kc, vc, out = _fused_step(w, pkv.PKV_VARIANT_AUTO)
+    d = _np(w)
+    rk, rv, ref = oracle_step(w, d, requests=req)
+    assert np.array_equal(as_numpy(kc), rk) and np.array_equal(as_numpy(vc), rv)
+    e = _err(out, ref, req)
+    _log(f"{name} full decode step err={e:.2e}")
+    assert e <= TOL
+    _, _, sep = gpu_step(w)
+    assert np.array_equal(out, sep)
+
+
 def test_shared_prefix_layers_sampled():
     w = make_workload("shared_prefix", layers=2)
     for layer in range(2):
