@@ -488,7 +488,7 @@ __global__ __launch_bounds__(64 * HW, 2) void decode_mfma_flat_kernel(DecodeArgs
     int jb, je;
     seg_bounds(cur, jb, je);
     new_row_place(a, n_raw0, jb, je, nr);
-    new_row_load(a, L, cur.b, cur.h, nr);
+    if (nr.blk >= 0) new_row_load(a, L, cur.b, cur.h, nr);
   }
   issue(kbuf[0], vbuf[0], __builtin_amdgcn_readlane(win0, 0), cur.h);
   issue(kbuf[1], vbuf[1], cur.nblk > 1 ? __builtin_amdgcn_readlane(win0, 1) : 0,
@@ -585,7 +585,15 @@ __global__ __launch_bounds__(64 * HW, 2) void decode_mfma_flat_kernel(DecodeArgs
           // row) go out between its first two blocks, so every wait for
           // them is one the first block needs anyway
           load_q<NG>(a, L, nxt.b, nxt.h, qop);
-          if constexpr (FUSED) new_row_load(a, L, nxt.b, nxt.h, nr);
+          if constexpr (FUSED) {
+            // this sequence's row is in place (its block came earlier in
+            // the group): place the next one, and load it only where it is
+            // this wave's to append
+            int jb2, je2;
+            seg_bounds(nxt, jb2, je2);
+            new_row_place(a, n_raw_nxt, jb2, je2, nr);
+            if (nr.blk >= 0) new_row_load(a, L, nxt.b, nxt.h, nr);
+          }
         }
         // the load of step i + 2, into the buffer this step has used
         const int j = i + 2;
@@ -643,14 +651,7 @@ __global__ __launch_bounds__(64 * HW, 2) void decode_mfma_flat_kernel(DecodeArgs
         const size_t base = (static_cast<size_t>(w) * 2 + slot) * a.g;
         write_state<NG>(acc, L, a.g, nullptr, part_o + base * kD, kD, part_ml + base * 2, 2);
       }
-      if (new_seq) {
-        acc_init<NG>(acc);
-        if constexpr (FUSED) {
-          int jb2, je2;
-          seg_bounds(nxt, jb2, je2);
-          new_row_place(a, n_raw_nxt, jb2, je2, nr);
-        }
-      }
+      if (new_seq) acc_init<NG>(acc);
     }
     return more;
   };
