@@ -523,16 +523,21 @@ __global__ __launch_bounds__(64 * HW, 2) void decode_mfma_flat_kernel(DecodeArgs
     const int nsteps = (c.nblk + 1) & ~1;
     int lim[NG];
     Half<NG> half[2];
-    int i0 = 0;
-    do {
+    // One pair of steps.  The pairs before a group's last are full blocks of
+    // the sequence (its last block, the only partial one and the one that
+    // holds the newest position, can only end a group), so only the last
+    // pair masks, substitutes the new row and sends the next sequence's
+    // queries: the steady-state body has none of those branches.
+    auto pair = [&](int i0, auto last_pair) {
+      constexpr bool LAST = decltype(last_pair)::value;
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         const int i = i0 + u;
         const int t0 = (jb + i) * kBS;
-        const int valid = i < c.nblk ? n - t0 : 0;
+        const int valid = !LAST ? kBS : i < c.nblk ? n - t0 : 0;
 #pragma unroll
         for (int G = 0; G < NG; ++G) lim[G] = valid - 1;
-        if constexpr (FUSED) {
+        if constexpr (FUSED && LAST) {
           if (jb + i == nr.blk) {  // uniform: the block that holds the new row
             // its id, from the window the walk loads it with (and, for fp8,
             // its scales, loaded with the tile)
@@ -580,7 +585,7 @@ __global__ __launch_bounds__(64 * HW, 2) void decode_mfma_flat_kernel(DecodeArgs
         qk_block<KV, NG>(a.scale_log2, L, lds_k, qop, kbuf[u], vbuf[u], valid, valid >= kBS,
                          lim, half[u]);
         if (u == 1) softmax_pv_pair<KV, NG>(half[0], half[1], acc);
-        if (u == 1 && i == nsteps - 1 && new_seq) {
+        if (LAST && u == 1 && new_seq) {
           // the group's last QK is done: the next sequence's Q (and new
           // row) go out between its first two blocks, so every wait for
           // them is one the first block needs anyway
@@ -610,8 +615,10 @@ __global__ __launch_bounds__(64 * HW, 2) void decode_mfma_flat_kernel(DecodeArgs
         }
         issue(kbuf[u], vbuf[u], p, hh);
       }
-      i0 += 2;
-    } while (i0 < nsteps);
+    };
+    int i0 = 0;
+    for (; i0 + 2 < nsteps; i0 += 2) pair(i0, std::false_type{});
+    pair(i0, std::true_type{});
     if (!more || new_seq) {
       // the sequence's part in this wave's range is done; what is written
       // follows the workgroup's chunk [lo, hi)
