@@ -520,6 +520,23 @@ def decode_measure(args, name, dev, full=True):
     torch.cuda.synchronize()
     ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
 
+    # timed region 3 (reported beside the headline, not used for it): the
+    # spread of single steps, one HIP event recorded between consecutive
+    # steps on the step's stream, so each interval also holds one event
+    # record
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    torch.cuda.synchronize()
+    ev[0].record(stream)
+    for i in range(args.steps):
+        step(i % R)
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    per = sorted(ev[i].elapsed_time(ev[i + 1]) * 1e3 / w.layers for i in range(args.steps))
+    pick = lambda f: per[min(len(per) - 1, int(round(f * (len(per) - 1))))]
+    step_dist = {"p10": round(pick(0.1), 2), "p50": round(pick(0.5), 2),
+                 "p90": round(pick(0.9), 2), "unit": "us per layer",
+                 "method": f"{args.steps} single steps between HIP events on the stream"}
+
     # timed region 2: the partition kernel alone, launched back to back over
     # the rotating pool copies, one HIP event pair on its stream around the
     # whole batch (per-launch event pairs would add the dispatch latency of
@@ -563,7 +580,8 @@ def decode_measure(args, name, dev, full=True):
         f"{100 * value / PEAK_GBS:.1f}% of peak; partition kernel avg "
         f"{kern_avg_ms * 1e3:.1f} us (batches: {', '.join(f'{x * 1e3:.1f}' for x in kern_ms)}); "
         f"KV bytes/layer {att['kv']}; kernel {achieved:.0f} GB/s = "
-        f"{100 * achieved / PEAK_GBS:.1f}% of peak")
+        f"{100 * achieved / PEAK_GBS:.1f}% of peak; single steps p10/p50/p90 "
+        f"{step_dist['p10']}/{step_dist['p50']}/{step_dist['p90']} us/layer")
     kernel = {0: "decode_mfma_flat_kernel", 1: "decode_generic_kernel",
               2: "decode_mfma_flat_kernel", 3: "decode_mfma_kernel"}[args.variant]
     if cascade:
@@ -579,7 +597,8 @@ def decode_measure(args, name, dev, full=True):
                       "logical_bytes_per_layer": logical_bytes,
                       "mean_context": round(sum(lens) / len(lens), 1),
                       "us_per_step_per_layer": round(ms_per_step * 1e3 / w.layers, 2),
-                      "pct_of_peak_step": round(100 * value / PEAK_GBS, 2)},
+                      "pct_of_peak_step": round(100 * value / PEAK_GBS, 2),
+                      "step_us_per_layer_spread": step_dist},
            "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_GBS,
                         "unit": "GB/s", "frac": round(achieved / PEAK_GBS, 4),
                         "traffic": traffic, "kernel": kernel,
@@ -654,8 +673,8 @@ def decode_measure(args, name, dev, full=True):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="llama8b")
     ap.add_argument("--also", default="long32k",
                     help="comma-separated decode workloads measured in the same run as "
@@ -735,6 +754,7 @@ def main():
         also[name] = {"us_per_step_per_layer": sub["config"]["us_per_step_per_layer"],
                       "step_gbs": sub["value"],
                       "pct_of_peak_step": sub["config"]["pct_of_peak_step"],
+                      "step_us_per_layer_spread": sub["config"]["step_us_per_layer_spread"],
                       "kernel_us": sub["roofline"]["avg_launch_us"],
                       "kernel_gbs": sub["roofline"]["achieved"],
                       "kernel_frac": sub["roofline"]["frac"],
