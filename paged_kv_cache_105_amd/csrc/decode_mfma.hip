@@ -846,12 +846,16 @@ int mfma_flat_waves(int kv_dtype, int g, int B, bool cascade) {
   }
   // per_cu counts workgroups (chunks) of waves_per_group waves.  Waves per
   // SIMD: one for bf16, and for two head groups with one wave per chunk;
-  // two for fp8 split chunks; what the occupancy allows for fp8 with one
-  // head group and one wave per chunk.
+  // what the occupancy allows for the other fp8 walks (split chunks with
+  // two head groups: two; with one: three; one wave per chunk: three).
+  // Measured on MI355X, fp8 GQA (four waves per chunk) with 512 / 640 / 768
+  // chunks: kernel 152.8-153.2 / 166.7 (uneven: some CUs hold three, some
+  // two) / 151.3-151.4 us, step 167.1-167.3 / 181.3-181.6 / 164.5-165.9 us;
+  // on another box, 512 vs 768: kernel 151.6-152.3 vs 151.4-152.0 us, step
+  // 165.0-165.7 vs 164.6-165.2 us.
   const int simds_per_cu = 4;
   int per_simd = 0;  // 0: the occupancy
   if (kv_dtype == DT_BF16 || (g > 16 && k.waves_per_group == 1)) per_simd = 1;
-  else if (k.waves_per_group > 1) per_simd = 2;
   if (per_simd > 0) {
     const int cap = simds_per_cu * per_simd / k.waves_per_group;
     per_cu = per_cu < cap ? per_cu : cap;
