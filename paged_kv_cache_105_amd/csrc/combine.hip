@@ -9,7 +9,8 @@
 // request (page 1 "KV cache: Generation state, latency, and allocation",
 // section 21.1); only the order of additions changes.
 //
-// One wave per (query head, request).  The workspace header says which
+// One wave per (query head, request), or per two query heads of one KV head
+// (combine_pair_kernel, below).  The workspace header says which
 // layout the partition kernel wrote (see pkv_device.h).  Requests whose
 // result the partition kernel wrote directly are skipped.  In a cascade
 // over a shared prefix (prefix_splits > 0, flat layout only) every request
@@ -66,6 +67,107 @@ __device__ inline void lse_merge(float& m, float& l, float m2, float l2) {
 
 }  // namespace
 
+// Where the pieces of (request b, query head hq) are.  Piece k < P1 has its
+// (m, l) at ml + k * ml_step and its o at o + k * o_step, piece 0 shifted by
+// (ml_first, o_first); a cascade's prefix pieces k = P1 .. P - 1 follow at
+// ml2, o2.
+struct PieceSet {
+  const float* ml = nullptr;
+  const float* o = nullptr;
+  const float* ml2 = nullptr;
+  const float* o2 = nullptr;
+  size_t ml_step = 2, o_step = 0, ml_first = 0, o_first = 0, ml2_step = 0, o2_step = 0;
+  int P1 = 0, P = 0;
+  __device__ const float* ml_at(int k) const {
+    return k < P1 ? ml + k * ml_step + (k == 0 ? ml_first : 0) : ml2 + (k - P1) * ml2_step;
+  }
+  __device__ const float* o_at(int k) const {
+    return k < P1 ? o + k * o_step + (k == 0 ? o_first : 0) : o2 + (k - P1) * o2_step;
+  }
+};
+
+// Locate the pieces of (b, hq); false when there is nothing to merge (the
+// attention launch wrote the row final, or the request is empty).  One round
+// trip for everything the lookup needs: the header, this request's length
+// and (flat layout) the block prefix, which starts right after the header;
+// the prefix words are read whenever they lie inside the workspace, whatever
+// the layout, and used only for the flat one.  Every value but the head's
+// own offsets is the same for all query heads of one KV head.
+__device__ __forceinline__ bool locate_pieces(const int32_t* __restrict__ context_lens,
+                                              const char* __restrict__ ws, size_t ws_bytes,
+                                              int B, int b, int hq, int H_Q, int H_KV, int d_h,
+                                              int partition_tokens, int max_parts,
+                                              int prefix_splits, PieceSet& ps) {
+  const WsHeader hd = *reinterpret_cast<const WsHeader*>(ws);
+  const int n_b = context_lens[b];
+  int pre_b = 0, pre_b1 = 0, pre_B = 0;
+  if (kWsHeader + sizeof(int32_t) * (static_cast<size_t>(B) + 1) <= ws_bytes) {
+    const int32_t* pre = reinterpret_cast<const int32_t*>(ws + kWsHeader);
+    pre_b = pre[b];
+    pre_b1 = pre[b + 1];
+    pre_B = pre[B];
+  }
+  int P = 0, P2 = 0;
+  ps.o_step = d_h;  // partition layout: pieces are contiguous
+  if (hd.mode == kWsPartition) {
+    P = min((n_b + partition_tokens - 1) / partition_tokens, max_parts);
+    if (P <= 1) return false;
+    const PartitionLayout PL = partition_layout(B, H_Q, max_parts, d_h);
+    const size_t base = (static_cast<size_t>(b) * H_Q + hq) * max_parts;
+    ps.ml = reinterpret_cast<const float*>(ws + PL.ml) + 2 * base;
+    ps.o = reinterpret_cast<const float*>(ws + PL.o) + base * d_h;
+  } else if (hd.mode == kWsFlat) {
+    // flat layout: pieces come from consecutive waves, each in slot 0 except
+    // the first wave's piece when that wave started in an earlier sequence
+    const int W = hd.waves, C = hd.chunks, g = hd.g;
+    const int h = hq / g, j = hq % g;
+    const FlatLayout FL = flat_layout(B, W, g, d_h);
+    const int nb = pre_b1 - pre_b;  // (a cascade: private blocks only)
+    const size_t rowi = static_cast<size_t>(b) * H_Q + hq;
+    if (prefix_splits > 0) {
+      if (n_b < 1) return false;
+      const CascadeLayout CL = cascade_layout(B, H_Q, W, g, d_h, prefix_splits);
+      const size_t rows = static_cast<size_t>(B) * H_Q;
+      P2 = prefix_splits;
+      ps.ml2 = reinterpret_cast<const float*>(ws + CL.pre_ml) + 2 * rowi;
+      ps.o2 = reinterpret_cast<const float*>(ws + CL.pre_o) + rowi * d_h;
+      ps.ml2_step = 2 * rows;
+      ps.o2_step = rows * d_h;
+      // the private part: one piece for an uncut sequence (below), else as
+      // in the plain layout
+      ps.ml = reinterpret_cast<const float*>(ws + CL.seq_ml) + 2 * rowi;
+      ps.o = reinterpret_cast<const float*>(ws + CL.seq_o) + rowi * d_h;
+      P = nb > 0 ? 1 : 0;
+    } else if (nb <= 0) {
+      return false;
+    }
+    if (nb > 0) {
+      const long long T = static_cast<long long>(H_KV) * pre_B;
+      const long long S = static_cast<long long>(H_KV) * pre_b + static_cast<long long>(h) * nb;
+      const int first_wave = flat_wave_of(S, T, C);
+      const int last_wave = flat_wave_of(S + nb - 1, T, C);
+      if (first_wave == last_wave) {
+        if (prefix_splits == 0) return false;  // written final by its wave
+      } else {
+        const int first_slot = flat_chunk_lo(first_wave, T, C) == S ? 0 : 1;
+        P = last_wave - first_wave + 1;
+        const size_t base = (static_cast<size_t>(first_wave) * 2) * g + j;
+        ps.ml = reinterpret_cast<const float*>(ws + FL.ml) + 2 * base;
+        ps.o = reinterpret_cast<const float*>(ws + FL.o) + base * d_h;
+        ps.ml_step = 2 * 2 * static_cast<size_t>(g);
+        ps.o_step = 2 * static_cast<size_t>(g) * d_h;
+        ps.ml_first = 2 * static_cast<size_t>(first_slot) * g;
+        ps.o_first = static_cast<size_t>(first_slot) * g * d_h;
+      }
+    }
+  } else {
+    return false;
+  }
+  ps.P1 = P;
+  ps.P = P + P2;
+  return true;
+}
+
 // VW: floats per vector load (4 when d_h % 4 == 0, else 1).  R: vector
 // columns per lane when a row has more than 64 of them (only VW = 1).
 template <int VW, int R>
@@ -80,93 +182,13 @@ __global__ __launch_bounds__(64) void combine_kernel(float* __restrict__ out,
   const int hq = blockIdx.x, b = blockIdx.y, B = gridDim.y, lane = threadIdx.x;
   float* dst = out + (static_cast<size_t>(b) * H_Q + hq) * d_h;
 
-  // One round trip for everything the piece lookup needs: the header, this
-  // request's length and (flat layout) the block prefix, which starts right
-  // after the header; the prefix words are read whenever they lie inside the
-  // workspace, whatever the layout, and used only for the flat one.
-  const WsHeader hd = *reinterpret_cast<const WsHeader*>(ws);
-  const int n_b = context_lens[b];
-  int pre_b = 0, pre_b1 = 0, pre_B = 0;
-  if (kWsHeader + sizeof(int32_t) * (static_cast<size_t>(B) + 1) <= ws_bytes) {
-    const int32_t* pre = reinterpret_cast<const int32_t*>(ws + kWsHeader);
-    pre_b = pre[b];
-    pre_b1 = pre[b + 1];
-    pre_B = pre[B];
-  }
-
-  // Locate the pieces: piece k (k < P) has its (m, l) at ml + k * ml_step
-  // and its o at o + k * o_step, piece 0 shifted by (ml_first, o_first);
-  // a cascade's prefix pieces k = P .. P + P2 - 1 follow at ml2, o2.
-  int P = 0, P2 = 0;
-  const float* ml = nullptr;
-  const float* o = nullptr;
-  const float* ml2 = nullptr;
-  const float* o2 = nullptr;
-  size_t ml_step = 2, o_step = d_h;  // partition layout: pieces are contiguous
-  size_t ml_first = 0, o_first = 0;
-  size_t ml2_step = 0, o2_step = 0;
-  if (hd.mode == kWsPartition) {
-    P = min((n_b + partition_tokens - 1) / partition_tokens, max_parts);
-    if (P <= 1) return;
-    const PartitionLayout PL = partition_layout(B, H_Q, max_parts, d_h);
-    const size_t base = (static_cast<size_t>(b) * H_Q + hq) * max_parts;
-    ml = reinterpret_cast<const float*>(ws + PL.ml) + 2 * base;
-    o = reinterpret_cast<const float*>(ws + PL.o) + base * d_h;
-  } else if (hd.mode == kWsFlat) {
-    // flat layout: pieces come from consecutive waves, each in slot 0 except
-    // the first wave's piece when that wave started in an earlier sequence
-    const int W = hd.waves, C = hd.chunks, g = hd.g;
-    const int h = hq / g, j = hq % g;
-    const FlatLayout FL = flat_layout(B, W, g, d_h);
-    const int nb = pre_b1 - pre_b;  // (a cascade: private blocks only)
-    const size_t rowi = static_cast<size_t>(b) * H_Q + hq;
-    if (prefix_splits > 0) {
-      if (n_b < 1) return;
-      const CascadeLayout CL = cascade_layout(B, H_Q, W, g, d_h, prefix_splits);
-      const size_t rows = static_cast<size_t>(B) * H_Q;
-      P2 = prefix_splits;
-      ml2 = reinterpret_cast<const float*>(ws + CL.pre_ml) + 2 * rowi;
-      o2 = reinterpret_cast<const float*>(ws + CL.pre_o) + rowi * d_h;
-      ml2_step = 2 * rows;
-      o2_step = rows * d_h;
-      // the private part: one piece for an uncut sequence (below), else as
-      // in the plain layout
-      ml = reinterpret_cast<const float*>(ws + CL.seq_ml) + 2 * rowi;
-      o = reinterpret_cast<const float*>(ws + CL.seq_o) + rowi * d_h;
-      P = nb > 0 ? 1 : 0;
-    } else if (nb <= 0) {
-      return;
-    }
-    if (nb > 0) {
-      const long long T = static_cast<long long>(H_KV) * pre_B;
-      const long long S = static_cast<long long>(H_KV) * pre_b + static_cast<long long>(h) * nb;
-      const int first_wave = flat_wave_of(S, T, C);
-      const int last_wave = flat_wave_of(S + nb - 1, T, C);
-      if (first_wave == last_wave) {
-        if (prefix_splits == 0) return;  // written final by its wave
-      } else {
-        const int first_slot = flat_chunk_lo(first_wave, T, C) == S ? 0 : 1;
-        P = last_wave - first_wave + 1;
-        const size_t base = (static_cast<size_t>(first_wave) * 2) * g + j;
-        ml = reinterpret_cast<const float*>(ws + FL.ml) + 2 * base;
-        o = reinterpret_cast<const float*>(ws + FL.o) + base * d_h;
-        ml_step = 2 * 2 * static_cast<size_t>(g);
-        o_step = 2 * static_cast<size_t>(g) * d_h;
-        ml_first = 2 * static_cast<size_t>(first_slot) * g;
-        o_first = static_cast<size_t>(first_slot) * g * d_h;
-      }
-    }
-  } else {
+  PieceSet ps;
+  if (!locate_pieces(context_lens, ws, ws_bytes, B, b, hq, H_Q, H_KV, d_h, partition_tokens,
+                     max_parts, prefix_splits, ps))
     return;
-  }
-  const int P1 = P;
-  auto ml_at = [=](int k) {
-    return k < P1 ? ml + k * ml_step + (k == 0 ? ml_first : 0) : ml2 + (k - P1) * ml2_step;
-  };
-  auto o_at = [=](int k) {
-    return k < P1 ? o + k * o_step + (k == 0 ? o_first : 0) : o2 + (k - P1) * o2_step;
-  };
-  P += P2;
+  const int P = ps.P;
+  auto ml_at = [&](int k) { return ps.ml_at(k); };
+  auto o_at = [&](int k) { return ps.o_at(k); };
 
   // pass 2's lane layout: lanes are split into PPI groups of LP lanes; group
   // s reads piece i * PPI + s of a chunk of 64 pieces on iteration i, lane c
@@ -268,11 +290,96 @@ __global__ __launch_bounds__(64) void combine_kernel(float* __restrict__ out,
   }
 }
 
+// Two query heads per wave, for d_h = 128 (a head's row is 32 vectors of 4
+// floats: half a wave) and an even group size: half s merges head
+// 2 * blockIdx.x + s.  Both heads read the same KV head and so have the same
+// pieces, so the lookup is done once for both and the wave count halves;
+// with many (request, head) rows the waves share SIMDs, and the per-wave
+// instructions are what the launch waits for.
+__global__ __launch_bounds__(64) void combine_pair_kernel(float* __restrict__ out,
+                                                          const int32_t* __restrict__ context_lens,
+                                                          const char* __restrict__ ws,
+                                                          size_t ws_bytes, int H_Q, int H_KV,
+                                                          int partition_tokens, int max_parts,
+                                                          int prefix_splits) {
+  using Vec = typename VecT<4>::type;
+  constexpr int kDh = 128;
+  const int lane = threadIdx.x, s = lane >> 5, c = lane & 31;
+  const int hq = 2 * blockIdx.x + s, b = blockIdx.y, B = gridDim.y;
+  PieceSet ps;
+  if (!locate_pieces(context_lens, ws, ws_bytes, B, b, hq, H_Q, H_KV, kDh, partition_tokens,
+                     max_parts, prefix_splits, ps))
+    return;  // the same for both halves: they share the sequence
+  const int P = ps.P;
+  // the rows of the first kUnroll pieces go out with the (m, l) loads
+  Vec x0[kUnroll];
+#pragma unroll
+  for (int u = 0; u < kUnroll; ++u)
+    x0[u] = u < P ? reinterpret_cast<const Vec*>(ps.o_at(u))[c] : Vec(0.f);
+
+  // pass 1: lane c of each half merges its head's pieces c, c + 32, ...
+  float m_own = -INFINITY, m_lane = -INFINITY, l_lane = 0.f;
+  if (c < P) {
+    const float2 x = *reinterpret_cast<const float2*>(ps.ml_at(c));
+    m_own = m_lane = x.x;
+    l_lane = x.y;
+  }
+  for (int k = c + 32; k < P; k += 32) {
+    const float2 x = *reinterpret_cast<const float2*>(ps.ml_at(k));
+    lse_merge(m_lane, l_lane, x.x, x.y);
+  }
+  for (int off = 16; off > 0; off >>= 1) {  // within the half
+    const float m2 = __shfl_xor(m_lane, off, 64), l2 = __shfl_xor(l_lane, off, 64);
+    lse_merge(m_lane, l_lane, m2, l2);
+  }
+  const float M = m_lane, inv = 1.0f / l_lane;
+
+  // pass 2: the weight of piece k0 + k is held by lane k of the half
+  Vec acc = Vec(0.f);
+  for (int k0 = 0; k0 < P; k0 += 32) {
+    const int kn = min(32, P - k0);
+    const float mk = (k0 == 0) ? m_own : (c < kn ? ps.ml_at(k0 + c)[0] : -INFINITY);
+    const float w = c < kn ? __builtin_amdgcn_exp2f(mk - M) * inv : 0.f;
+    for (int i0 = 0; i0 < kn; i0 += kUnroll) {
+      Vec x[kUnroll];
+      float wk[kUnroll];
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const int kk = i0 + u;
+        const bool valid = kk < kn;
+        wk[u] = __shfl(w, 32 * s + (valid ? kk : 0), 64);
+        if (k0 == 0 && i0 == 0)
+          x[u] = x0[u];
+        else
+          x[u] = valid ? reinterpret_cast<const Vec*>(ps.o_at(k0 + kk))[c] : Vec(0.f);
+        if (!valid) wk[u] = 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) acc += wk[u] * x[u];
+    }
+  }
+  reinterpret_cast<Vec*>(out + (static_cast<size_t>(b) * H_Q + hq) * kDh)[c] = acc;
+}
+
 hipError_t launch_combine(float* out, const int32_t* context_lens, const void* ws,
                           size_t ws_bytes, int B, int H_Q, int H_KV, int d_h, int partition_tokens,
                           int max_parts, int prefix_splits, hipStream_t stream) {
-  const dim3 grid(H_Q, B), block(64);
   const char* w = static_cast<const char*>(ws);
+  // Two heads per wave where the rows are many and each has few pieces: with
+  // at least 128 (request, KV head) sequences the balanced split cuts each
+  // into a few pieces.  With few long sequences (the 32K batch: 64 of them,
+  // 17 pieces each) a whole wave per head keeps twice the loads in flight.
+  // Measured on MI355X, step us one head / two heads per wave: fp8 MQA
+  // 41.3-41.5 / 39.9-40.1, fp8 GQA 165.0-165.6 / 163.0-164.1, shared prefix
+  // 55.1-55.4 / 54.8 per layer, 8B batch 61.0-61.2 / 60.7-61.5, 32K batch
+  // 171.6-172.8 / 172.8-173.3.
+  if (d_h == 128 && (H_Q / H_KV) % 2 == 0 && static_cast<long long>(B) * H_KV >= 128) {
+    hipLaunchKernelGGL(combine_pair_kernel, dim3(H_Q / 2, B), dim3(64), 0, stream, out,
+                       context_lens, w, ws_bytes, H_Q, H_KV, partition_tokens, max_parts,
+                       prefix_splits);
+    return hipGetLastError();
+  }
+  const dim3 grid(H_Q, B), block(64);
 #define PKV_COMBINE(VW, R)                                                                    \
   hipLaunchKernelGGL((combine_kernel<VW, R>), grid, block, 0, stream, out, context_lens, w,        \
                      ws_bytes, H_Q, H_KV, d_h, partition_tokens, max_parts, prefix_splits)

@@ -597,6 +597,21 @@ def test_full_llama8b_all_requests():
     assert e <= TOL
 
 
+@pytest.mark.parametrize("variant,pt", [(pkv.PKV_VARIANT_MFMA_PARTITION, 256),
+                                        (pkv.PKV_VARIANT_GENERIC, 256)],
+                         ids=["mfma_part", "generic"])
+def test_full_llama8b_partition_layouts(variant, pt):
+    # the fixed-partition layout with many (request, KV head) rows, the case
+    # where the combine merges two query heads per wave: up to 17 pieces per
+    # row, every request against the oracle
+    w = make_workload("llama8b")
+    _, _, out = gpu_step(w, partition_tokens=pt, variant=variant)
+    _, _, ref = oracle_step(w, _np(w))
+    e = _err(out, ref)
+    _log(f"llama8b full, partition layout v={variant} pt={pt} err={e:.2e}")
+    assert e <= TOL
+
+
 @pytest.mark.parametrize("name,req", [("long32k", [0, 7]), ("fp8_gqa", [0, 5, 77, 127]),
                                       ("fp8_mqa", [1, 64, 126]), ("fp8_mha", [0, 63, 127])])
 def test_full_size_sampled(name, req):
