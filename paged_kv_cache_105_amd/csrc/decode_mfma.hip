@@ -717,7 +717,8 @@ __global__ __launch_bounds__(64 * HW, 2) void decode_mfma_flat_kernel(DecodeArgs
 // MQA 45.0-45.6 / 47.0-47.6; fp8 GQA (one head group, four waves per chunk)
 // 170.0-171.2 / 169.1-170.6, no gain (again 165.9-167.5 / 165.5-166.3 once
 // the split chunks ran three waves per SIMD: its fused kernel needs 171
-// registers, two waves); fp8 MHA would lose a wave per SIMD the same way
+// registers, two waves; held to 168 registers for three, with 4 spilled,
+// 171.1-172.5 / 164.9); fp8 MHA would lose a wave per SIMD the same way
 // (171 instead of 155 registers: two waves instead of three).
 bool mfma_fuses_append(int kv_dtype, int g, bool flat, bool cascade) {
   if (kv_dtype == DT_BF16) return g <= 16;
