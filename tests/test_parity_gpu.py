@@ -597,6 +597,45 @@ def test_full_llama8b_all_requests():
     assert e <= TOL
 
 
+def _random_shapes(n, seed):
+    # (name, overrides, sampled requests) with seeded random batch sizes,
+    # group sizes, KV heads and context lengths: among them batches at, just
+    # below and above 128 (request, KV head) sequences, odd group sizes, one
+    # request, contexts from 1 to 3000 positions
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        name = "llama8b" if i % 2 == 0 else "fp8_mqa"
+        H_KV = int(rng.choice([1, 2, 3, 4, 8]))
+        g = int(rng.choice([1, 2, 3, 4, 6, 8, 16, 24, 32]))
+        B = int(rng.choice([1, 7, 42, 127, 128, 129, 200])) if i % 3 else 128 // H_KV
+        lens = rng.integers(1, 3001, size=B).tolist()
+        req = sorted(set(int(x) for x in rng.choice(B, size=min(B, 4), replace=False)))
+        out.append((name, dict(lens_after=lens, H_Q=g * H_KV, H_KV=H_KV), req))
+    return out
+
+
+@pytest.mark.parametrize("name,kw,req", _random_shapes(16, 2026),
+                         ids=lambda x: str(x)[:24] if isinstance(x, str) else "")
+def test_random_shapes_decode_step(name, kw, req):
+    # pkv_decode_step on seeded random shapes (bf16 and fp8 caches): pools
+    # bit-exact, sampled outputs within tolerance, outputs bitwise equal to the
+    # separate append + attention calls
+    w = make_workload(name, **kw)
+    _log(f"random decode step {name} B={w.B} H_Q={w.H_Q} H_KV={w.H_KV} "
+         f"max_len={w.max_context_len} req={req}")
+    kc, vc, out = _fused_step(w, pkv.PKV_VARIANT_AUTO)
+    d = _np(w)
+    rk, rv, ref = oracle_step(w, d, requests=req)
+    assert np.array_equal(as_numpy(kc), rk) and np.array_equal(as_numpy(vc), rv)
+    e = _err(out, ref, req)
+    _log(f"random decode step err={e:.2e}")
+    assert e <= TOL
+    assert np.all(np.isfinite(out))
+    _, _, sep = gpu_step(w)
+    assert np.array_equal(out, sep)
+
+
 @pytest.mark.parametrize("variant,pt", [(pkv.PKV_VARIANT_MFMA_PARTITION, 256),
                                         (pkv.PKV_VARIANT_GENERIC, 256)],
                          ids=["mfma_part", "generic"])
