@@ -290,8 +290,10 @@ __global__ __launch_bounds__(64 * kWgWaves, 2) void chunk_mfma_wg_kernel(DecodeA
       for (int G = 0; G < NG; ++G) {
         const float mxa = fmax_fast(fmax_fast(sa[G][0], sa[G][1]), fmax_fast(sa[G][2], sa[G][3]));
         const float mxb = fmax_fast(fmax_fast(sb[G][0], sb[G][1]), fmax_fast(sb[G][2], sb[G][3]));
-        const float mx = colmax4(fmax_fast(mxa, mxb) * kscale);
-        if (__any(mx > acc.m[G] + kRescaleSlack)) {
+        // the column max only where the running max moves (see softmax_pv_pair)
+        const float ml = fmax_fast(mxa, mxb) * kscale;
+        if (__any(ml > acc.m[G] + kRescaleSlack)) {
+          const float mx = colmax4(ml);
           const float m_new = fmaxf(acc.m[G], mx);
           const float alpha = __builtin_amdgcn_exp2f(acc.m[G] - m_new);
           acc.l[G] *= alpha;

@@ -361,10 +361,15 @@ __device__ __forceinline__ void softmax_pv_pair(const Half<NG>& a, const Half<NG
         fmax_fast(fmax_fast(a.s2[G][0], a.s2[G][1]), fmax_fast(a.s2[G][2], a.s2[G][3]));
     const float mxb =
         fmax_fast(fmax_fast(b.s2[G][0], b.s2[G][1]), fmax_fast(b.s2[G][2], b.s2[G][3]));
-    const float mx = colmax4(fmax_fast(mxa * a.kscale, mxb * b.kscale));
     // raise the running max only when needed (uniform branch over the wave;
-    // the first real block always takes it since m starts at -inf)
-    if (__any(mx > acc.m[G] + kRescaleSlack)) {
+    // the first real block always takes it since m starts at -inf).  A
+    // column's max exceeds its running max by more than the slack exactly
+    // when one of its four lanes' values does, so the column max -- a
+    // reduction across lanes -- is only taken inside the branch, off the
+    // per-block chain.
+    const float ml = fmax_fast(mxa * a.kscale, mxb * b.kscale);
+    if (__any(ml > acc.m[G] + kRescaleSlack)) {
+      const float mx = colmax4(ml);
       const float m_new = fmaxf(acc.m[G], mx);
       const float alpha = __builtin_amdgcn_exp2f(acc.m[G] - m_new);
       acc.l[G] *= alpha;
