@@ -823,9 +823,9 @@ KernelPick pick_kernel(int kv_dtype, int g, bool flat, bool fused, bool cascade)
 }  // namespace
 
 // Grid size of the flat kernel: never more waves than fit on the device at
-// once.  bf16 blocks (8 KiB of K and V per KV head) stream best with one wave
-// per SIMD -- longer chunks amortise each wave's start (lengths, table, first
-// block) and fewer streams contend for HBM; fp8 blocks carry half the bytes
+// once.  bf16 blocks (8 KiB of K and V per KV head) stream best with two
+// waves per CU -- longer chunks amortise each wave's start (lengths, table,
+// first block) and fewer streams contend for HBM; fp8 blocks carry half the bytes
 // for the same matrix and softmax work, so with one head group they need
 // every resident wave to keep the memory busy.  With two head groups (g > 16)
 // every cut sequence writes 32 heads of partials (16.6 KiB per piece), so
@@ -848,19 +848,37 @@ int mfma_flat_waves(int kv_dtype, int g, int B, bool cascade) {
     return 256 * 4;
   }
   // per_cu counts workgroups (chunks) of waves_per_group waves.  Waves per
-  // SIMD: one for bf16, and for two head groups with one wave per chunk;
-  // what the occupancy allows for the other fp8 walks (split chunks with
-  // two head groups: two; with one: three; one wave per chunk: three).
+  // CU: two for bf16; one per SIMD for two head groups with one wave per
+  // chunk; what the occupancy allows for the other fp8 walks (split chunks
+  // with two head groups: two per SIMD; with one: three; one wave per chunk:
+  // three).
   // Measured on MI355X, fp8 GQA (four waves per chunk) with 512 / 640 / 768
   // chunks: kernel 152.8-153.2 / 166.7 (uneven: some CUs hold three, some
   // two) / 151.3-151.4 us, step 167.1-167.3 / 181.3-181.6 / 164.5-165.9 us;
   // on another box, 512 vs 768: kernel 151.6-152.3 vs 151.4-152.0 us, step
   // 165.0-165.7 vs 164.6-165.2 us.
+  //
+  // bf16 walks read best with two waves per CU, half the SIMDs: fewer,
+  // longer streams (and half as many cut sequences); a cascade keeps one
+  // wave per SIMD, since its prefix workgroups are bound by their score and
+  // P.V products (shared-prefix batch, kernel us with W = 512 / 640 / 768 /
+  // 896 / 1024 / 1152 / 1280: 50.8 / 49.6 / 48.9 / 50.6 / 48.8-48.9 / 53.5 /
+  // 51.2).  Measured on MI355X,
+  // kernel us with W = 256 / 320 / 384 / 448 / 512 / 576 / 640 / 704 / 768
+  // / 832 / 896 / 960 / 1024 / 1152 waves: 8B-style batch 80.4 / 67.9 /
+  // 59.0 / 53.6 / 51.2-51.5 / 53.9 / 53.7 / 53.0 / 52.3-52.6 / 56.4 / 54.2
+  // / 53.1 / 53.5-53.8 / 58.3, 32K batch 251.9 / 210.7 / 182.0 / 163.9 /
+  // 155.3-155.5 / 166.6 / 162.6 / 162.0 / 161.1-162.8 / 172.6 / 165.8 /
+  // 163.8 / 160.9-162.3 / 176.1 (grids that do not divide evenly over the
+  // CUs are slower).
   const int simds_per_cu = 4;
-  int per_simd = 0;  // 0: the occupancy
-  if (kv_dtype == DT_BF16 || (g > 16 && k.waves_per_group == 1)) per_simd = 1;
-  if (per_simd > 0) {
-    const int cap = simds_per_cu * per_simd / k.waves_per_group;
+  int cap_per_cu = 0;  // 0: the occupancy
+  if (kv_dtype == DT_BF16)
+    cap_per_cu = cascade ? simds_per_cu : 2;
+  else if (g > 16 && k.waves_per_group == 1)
+    cap_per_cu = simds_per_cu;
+  if (cap_per_cu > 0) {
+    const int cap = cap_per_cu / k.waves_per_group;
     per_cu = per_cu < cap ? per_cu : cap;
   }
   return cus * (per_cu > 0 ? per_cu : 1);
