@@ -10,7 +10,10 @@ rotate over ``--rotate`` copies of the KV pools (same tables, different
 buffers); the 32-layer workload rotates by itself.
 
 Prints ONE JSON line on stdout (diagnostics go to stderr).  ``value`` is the
-achieved algorithmic GB/s of the whole step; ``roofline`` reports the
+achieved algorithmic GB/s of the whole step, over exactly K timed steps
+between two synchronizations, timed by a HIP event pair on the stream around
+them (the host's wall clock over the same region is in
+``config.wall_us_per_step_per_layer``); ``roofline`` reports the
 partition kernel alone, timed with HIP events on the stream it runs on;
 ``cpu_baseline`` times the float64 CPU oracle on a bounded sample of the
 same workload, on one core and (``all_cores``) on every allowed core;
@@ -398,22 +401,18 @@ def chunk_main(args, w, dev):
 
     for i in range(args.warmup):
         step(i % R)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(i % R)
-    torch.cuda.synchronize()
-    ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    ms_per_step, wall_ms_per_step = timed_steps(step, args.steps, R, stream)
     kern_ms = []
+    n_kern = max(args.steps, 10)
     for rep in range(3):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         e0.record(stream)
-        for i in range(args.steps):
+        for i in range(n_kern):
             attend(i % R)
         e1.record(stream)
         torch.cuda.synchronize()
-        kern_ms.append(e0.elapsed_time(e1) / args.steps)
+        kern_ms.append(e0.elapsed_time(e1) / n_kern)
     kern_ms.sort()
     kern_avg_ms = kern_ms[len(kern_ms) // 2]
     flops = chunk_flops(lens, qs, w.H_Q, w.d_h)
@@ -445,7 +444,9 @@ def chunk_main(args, w, dev):
                    "d_h": w.d_h, "block_size": w.block_size, "kv_dtype": w.kv_dtype,
                    "q_dtype": w.q_dtype, "new_tokens": w.total_q,
                    "max_context": w.max_context_len, "shared_blocks": w.shared_blocks,
-                   "pool_copies": R, "us_per_step": round(ms_per_step * 1e3, 2)},
+                   "pool_copies": R, "us_per_step": round(ms_per_step * 1e3, 2),
+                   "step_timing": "HIP event pair on the stream around the K timed steps",
+                   "wall_us_per_step": round(wall_ms_per_step * 1e3, 2)},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": None, "kernel": kernel,
@@ -456,10 +457,29 @@ def chunk_main(args, w, dev):
     print(json.dumps(res), flush=True)
 
 
+def timed_steps(step, steps, R, stream):
+    """Run exactly ``steps`` steps (step(i) for pool copy i % R) between two
+    synchronizations; returns (ms per step from a HIP event pair on
+    ``stream`` around them, ms per step by the host's wall clock over the
+    same region)."""
+    import torch
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for i in range(steps):
+        step(i % R)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3 / steps
+    return e0.elapsed_time(e1) / steps, wall
+
+
 def decode_measure(args, name, dev, full=True):
     """Measure one decode workload: the step (append + attention + combine)
-    by wall clock over args.steps steps, and the partition kernel alone by
-    HIP events around back-to-back launches on its stream.  With ``full``,
+    over exactly args.steps steps (HIP events on the stream, and the host's
+    wall clock beside them), and the partition kernel alone by HIP events
+    around back-to-back launches on its stream.  With ``full``,
     also the reference bandwidths of plain kernels on this machine, the
     compute-free gather of the same tiles, and the optional block-copy and
     calibration measurements.  Returns (record, workload, pools)."""
@@ -519,12 +539,13 @@ def decode_measure(args, name, dev, full=True):
         step(i % R)
     torch.cuda.synchronize()
 
-    # timed region 1: wall clock over K steps, no extra events
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(i % R)
-    torch.cuda.synchronize()
-    ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    # timed region 1: exactly K steps between two synchronizations, timed by
+    # one HIP event pair on the step's stream around them (the time the GPU
+    # spends on the K steps).  The host's wall clock over the same region is
+    # reported beside it: it also holds the GPU's start from idle and the
+    # final synchronization's wake-up, a fixed ~0.1 ms that weighs on short
+    # runs (20 steps: ~7 us per step).
+    ms_per_step, wall_ms_per_step = timed_steps(step, args.steps, R, stream)
 
     # timed region 3 (reported beside the headline, not used for it): the
     # spread of single steps, one HIP event recorded between consecutive
@@ -546,13 +567,15 @@ def decode_measure(args, name, dev, full=True):
     # timed region 2: the partition kernel alone, launched back to back over
     # the rotating pool copies, one HIP event pair on its stream around the
     # whole batch (per-launch event pairs would add the dispatch latency of
-    # each launch to its time)
+    # each launch to its time); at least 100 launches per batch, so the
+    # start of a batch from an idle GPU weighs little
     kern_ms = []
+    n_kern = max(args.steps, 100)
     for rep in range(3):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         e0.record(stream)
-        for i in range(args.steps):
+        for i in range(n_kern):
             for L in range(w.layers):
                 kc, vc = pools[i % R][L]
                 if cascade:
@@ -565,7 +588,7 @@ def decode_measure(args, name, dev, full=True):
                                           partition_tokens=pt, workspace=work, stream=stream)
         e1.record(stream)
         torch.cuda.synchronize()
-        kern_ms.append(e0.elapsed_time(e1) / (args.steps * w.layers))
+        kern_ms.append(e0.elapsed_time(e1) / (n_kern * w.layers))
     kern_ms.sort()
     kern_avg_ms = kern_ms[len(kern_ms) // 2]
 
@@ -604,6 +627,8 @@ def decode_measure(args, name, dev, full=True):
                       "mean_context": round(sum(lens) / len(lens), 1),
                       "us_per_step_per_layer": round(ms_per_step * 1e3 / w.layers, 2),
                       "pct_of_peak_step": round(100 * value / PEAK_GBS, 2),
+                      "step_timing": "HIP event pair on the stream around the K timed steps",
+                      "wall_us_per_step_per_layer": round(wall_ms_per_step * 1e3 / w.layers, 2),
                       "step_us_per_layer_spread": step_dist},
            "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_GBS,
                         "unit": "GB/s", "frac": round(achieved / PEAK_GBS, 4),
@@ -635,7 +660,7 @@ def decode_measure(args, name, dev, full=True):
     del x, y
     log(f"reference torch kernels: {ref}")
 
-    ref["gather_gbs"] = gather_reference(w, pools, stream, args.steps)
+    ref["gather_gbs"] = gather_reference(w, pools, stream, max(args.steps, 100))
     log(f"compute-free gather of the same tiles: {ref['gather_gbs']} GB/s "
         f"(partition kernel at {100 * achieved / ref['gather_gbs']:.1f}% of it)")
 
