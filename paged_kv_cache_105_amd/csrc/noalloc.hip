@@ -19,8 +19,9 @@
 namespace {
 
 // Upper bound of the step's workspace: the partial results of the split
-// (e.g. 4.3 MB for 32 requests of 32 query heads, 34 MB for 32 query heads
-// sharing one KV head on 1,024 waves).  Shapes that need more are refused.
+// (e.g. 2.1 MB for 32 requests of 32 query heads on 8 KV heads, 8.5 MB for
+// 128 requests of 32 query heads sharing one KV head).  Shapes that need
+// more are refused.
 constexpr size_t kScratchBytes = PKV_NOALLOC_SCRATCH_BYTES;
 static_assert(kScratchBytes % 256 == 0, "whole 256-byte units");
 
