@@ -343,10 +343,10 @@ __global__ __launch_bounds__(64 * HW, 2) void decode_mfma_flat_kernel(DecodeArgs
   const int skip = a.cascade ? a.shared_blocks : 0;
   int carry = 0;
   int x = 0;  // lane l ends with prefix[b0 + l + 1] of the last 64 requests
-  for (int b0 = 0; b0 < B; b0 += 64) {
+  // one slice of 64 requests: n = their lengths (lane l: request b0 + l)
+  auto scan_slice = [&](int b0, int n) {
     const int b = b0 + L.lane;
-    int nb = 0;
-    if (b < B) nb = min(max(a.context_lens[b], 0), cap * kBS);
+    int nb = b < B ? min(max(n, 0), cap * kBS) : 0;
     nb = max((nb + kBS - 1) / kBS - skip, 0);
     x = nb;  // inclusive scan across the wave
 #pragma unroll
@@ -357,6 +357,25 @@ __global__ __launch_bounds__(64 * HW, 2) void decode_mfma_flat_kernel(DecodeArgs
     x += carry;
     if (hw == 0 && b < B) prefix[b + 1] = x;  // every wave holds the same x
     carry = __builtin_amdgcn_readlane(x, 63);
+  };
+  constexpr int kSlices = 4;
+  if (B <= 64 * kSlices) {
+    // the lengths of up to 256 requests load together, so the walk waits
+    // for one round trip to memory rather than one per slice
+    int n[kSlices];
+#pragma unroll
+    for (int s = 0; s < kSlices; ++s) {
+      const int b = s * 64 + L.lane;
+      n[s] = b < B ? a.context_lens[b] : 0;
+    }
+#pragma unroll
+    for (int s = 0; s < kSlices; ++s)
+      if (s * 64 < B) scan_slice(s * 64, n[s]);
+  } else {
+    for (int b0 = 0; b0 < B; b0 += 64) {
+      const int b = b0 + L.lane;
+      scan_slice(b0, b < B ? a.context_lens[b] : 0);
+    }
   }
   if (hw == 0 && L.lane == 0) prefix[0] = 0;
   if constexpr (HW > 1) {

@@ -196,6 +196,24 @@ def test_decode_step_fused_append(variant, name, kw):
     assert np.array_equal(out, sep)
 
 
+@pytest.mark.parametrize("B", [64, 65, 200, 256, 257, 300])
+@pytest.mark.parametrize("name,kw", [("llama8b", dict(H_Q=8, H_KV=2)), ("fp8_mqa", {})],
+                         ids=["bf16_g4", "fp8_mqa"])
+def test_batches_past_64_requests(B, name, kw):
+    # the balanced split's block prefix reads the lengths 64 requests at a
+    # time: up to four slices together, one after another past 256 requests.
+    # The lengths cycle, so every slice holds one-position requests and
+    # requests on both sides of a block boundary.
+    lens = [(1, 5, 16, 17, 40, 70, 33)[i % 7] for i in range(B)]
+    w = make_workload(name, lens_after=lens, **kw)
+    _, _, ref = oracle_step(w, _np(w))
+    _, _, out = gpu_step(w, variant=pkv.PKV_VARIANT_MFMA)
+    _, _, fused = _fused_step(w, pkv.PKV_VARIANT_MFMA)
+    e, ef = _err(out, ref), _err(fused, ref)
+    _log(f"{name} B={B} err={e:.2e} fused err={ef:.2e}")
+    assert e <= TOL and ef <= TOL
+
+
 def test_fp8_append_exhaustive_bf16_inputs():
     # every bf16 bit pattern (NaN and inf included) x 4 scales through the
     # append kernel; codes must equal the oracle's RNE + saturation encoder
